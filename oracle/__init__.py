@@ -1,0 +1,243 @@
+"""CPU oracle for the per-rank ZeRO-1 shard step (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The HIP library and its Python binding
+never import it, and the two share no code.
+
+The arithmetic lives in ``zero_oracle.c`` (plain sequential loops, binary32 for
+the rank fold that the step defines in binary32, binary64 elsewhere); this file
+only marshals numpy arrays through ctypes. See the header of ``zero_oracle.c``
+for the step, its order and the passages of the pages each part follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "zero_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libzero_oracle.so")
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no GPU code involved)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
+                ("max_grad_norm", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("skip_on_nonfinite", ctypes.c_int32)]
+
+
+class _Result(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("grad_norm", ctypes.c_double), ("clip_coef", ctypes.c_double),
+                ("found_inf", ctypes.c_int32), ("skipped", ctypes.c_int32)]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)),
+                ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("param_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = build()
+        L = ctypes.CDLL(path)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+        L.oracle_bf16_to_f32.argtypes = [vp, vp, i64]
+        L.oracle_f32_to_bf16.argtypes = [vp, vp, i64]
+        L.oracle_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, dbl, vp]
+        L.oracle_check.argtypes = [vp, i64, ctypes.POINTER(dbl), ctypes.POINTER(i32)]
+        L.oracle_finalize.argtypes = [dbl, dbl, i32, dbl, i32, ctypes.POINTER(_Result)]
+        L.oracle_adamw.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_Hparams), dbl]
+        L.oracle_zero_step.argtypes = [ctypes.POINTER(_Tensor), i32, i32, ctypes.POINTER(_Hparams), dbl,
+                                       ctypes.POINTER(_Result)]
+        L.oracle_zero_step.restype = i32
+        for f in ("oracle_bf16_to_f32", "oracle_f32_to_bf16", "oracle_reduce", "oracle_check",
+                  "oracle_finalize", "oracle_adamw"):
+            getattr(L, f).restype = None
+        _lib = L
+    return _lib
+
+
+@dataclasses.dataclass
+class HParams:
+    """AdamW knobs named as in the optimizer block of a deepspeed_config.json
+    ([5D post] 4.2), plus the step index, the clip threshold, the AMP gradient
+    multiplier and the skip switch."""
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+    step: int = 1
+    max_grad_norm: float = 0.0
+    grad_scale: float = 1.0
+    skip_on_nonfinite: int = 0
+
+    def _c(self) -> _Hparams:
+        return _Hparams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, int(self.step),
+                        self.max_grad_norm, self.grad_scale, int(self.skip_on_nonfinite))
+
+
+@dataclasses.dataclass
+class Result:
+    sumsq: float
+    grad_norm: float
+    clip_coef: float
+    found_inf: int
+    skipped: int
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.float32, a.dtype
+    return a
+
+
+def _p(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def bf16_to_f32(h) -> np.ndarray:
+    h = _u16(h)
+    out = np.empty(h.shape, np.float32)
+    lib().oracle_bf16_to_f32(_p(h), _p(out), h.size)
+    return out
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    x = _f32(x)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f32_to_bf16(_p(x), _p(out), x.size)
+    return out
+
+
+def reduce(grads: Sequence[np.ndarray], grad_scale: float = 1.0) -> np.ndarray:
+    """Ascending-rank binary32 fold of M bf16 replicas, times scale32."""
+    gs = [_u16(g) for g in grads]
+    n = gs[0].size
+    assert all(g.size == n for g in gs)
+    ptrs = (ctypes.c_void_p * len(gs))(*[_p(g) for g in gs])
+    out = np.empty(n, np.float32)
+    lib().oracle_reduce(ptrs, len(gs), n, float(grad_scale), _p(out))
+    return out
+
+
+def check(g, sumsq: float = 0.0, found_inf: int = 0):
+    g = _f32(g)
+    s = ctypes.c_double(sumsq)
+    f = ctypes.c_int32(found_inf)
+    lib().oracle_check(_p(g), g.size, ctypes.byref(s), ctypes.byref(f))
+    return s.value, f.value
+
+
+def finalize(sumsq: float, external_sumsq: float, found_inf: int, max_grad_norm: float,
+             skip_on_nonfinite: int) -> Result:
+    r = _Result()
+    lib().oracle_finalize(sumsq, external_sumsq, int(found_inf), max_grad_norm, int(skip_on_nonfinite),
+                          ctypes.byref(r))
+    return Result(r.sumsq, r.grad_norm, r.clip_coef, r.found_inf, r.skipped)
+
+
+def adamw(master, exp_avg, exp_avg_sq, g, hp: HParams, coef: float = 1.0):
+    """Returns new (master, exp_avg, exp_avg_sq, param_out); inputs untouched."""
+    th, m, v = _f32(master).copy(), _f32(exp_avg).copy(), _f32(exp_avg_sq).copy()
+    g = _f32(g)
+    out = np.empty(th.shape, np.uint16)
+    h = hp._c()
+    lib().oracle_adamw(_p(th), _p(m), _p(v), _p(g), _p(out), th.size, ctypes.byref(h), float(coef))
+    return th, m, v, out
+
+
+@dataclasses.dataclass
+class TensorState:
+    grads: list          # M arrays of uint16 (bf16 bits)
+    master: np.ndarray   # float32
+    exp_avg: np.ndarray  # float32
+    exp_avg_sq: np.ndarray  # float32
+    param_out: np.ndarray | None = None  # uint16; left as given on a skipped step
+
+
+def zero_step(tensors: Sequence[TensorState], hp: HParams, external_sumsq: float = 0.0):
+    """The whole step over a tensor list. Returns (new TensorStates, Result).
+    The inputs are not modified; a skipped step returns copies of the old state."""
+    T = len(tensors)
+    M = len(tensors[0].grads)
+    keep = []
+    cts = (_Tensor * max(T, 1))()
+    new = []
+    for i, t in enumerate(tensors):
+        gs = [_u16(g) for g in t.grads]
+        assert len(gs) == M
+        n = t.master.size
+        st = TensorState(gs, _f32(t.master).copy(), _f32(t.exp_avg).copy(), _f32(t.exp_avg_sq).copy(),
+                         (_u16(t.param_out).copy() if t.param_out is not None else np.zeros(n, np.uint16)))
+        ptrs = (ctypes.c_void_p * M)(*[_p(g) for g in gs])
+        keep.append(ptrs)
+        cts[i] = _Tensor(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), _p(st.master), _p(st.exp_avg),
+                         _p(st.exp_avg_sq), _p(st.param_out))
+        new.append(st)
+    h = hp._c()
+    r = _Result()
+    rc = lib().oracle_zero_step(cts, T, M, ctypes.byref(h), float(external_sumsq), ctypes.byref(r))
+    if rc != 0:
+        raise MemoryError("oracle_zero_step: out of host memory")
+    return new, Result(r.sumsq, r.grad_norm, r.clip_coef, r.found_inf, r.skipped)
+
+
+# --------------------------------------------------------------------------
+# Memory accounting of mixed-precision AdamW training state
+# ([CS336 L7] "训练内存的详细分析": bf16 parameter 2 B, bf16 gradient 2 B,
+# fp32 master 4 B, fp32 first moment 4 B, fp32 second moment 4 B per
+# parameter; [ZeRO ch.] 2.3.4 and [CS336 L7] "ZeRO Stage 1": the optimizer
+# state -- master, m, v -- is split 1/N across the N data-parallel ranks).
+# --------------------------------------------------------------------------
+
+BYTES_PER_PARAM = {"param_bf16": 2, "grad_bf16": 2, "master_fp32": 4, "exp_avg_fp32": 4, "exp_avg_sq_fp32": 4}
+
+
+def bytes_per_param_naive_dp() -> int:
+    return sum(BYTES_PER_PARAM.values())
+
+
+def bytes_per_gpu(n_params: float, n_ranks: int, stage: int) -> float:
+    """Per-GPU bytes of the training state for naive DP (stage 0) or ZeRO
+    stages 1-3 over n_ranks data-parallel ranks (activations excluded)."""
+    p = BYTES_PER_PARAM["param_bf16"]
+    g = BYTES_PER_PARAM["grad_bf16"]
+    opt = BYTES_PER_PARAM["master_fp32"] + BYTES_PER_PARAM["exp_avg_fp32"] + BYTES_PER_PARAM["exp_avg_sq_fp32"]
+    if stage == 0:
+        per = p + g + opt
+    elif stage == 1:
+        per = p + g + opt / n_ranks
+    elif stage == 2:
+        per = p + (g + opt) / n_ranks
+    elif stage == 3:
+        per = (p + g + opt) / n_ranks
+    else:
+        raise ValueError(stage)
+    return n_params * per

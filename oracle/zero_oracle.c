@@ -1,0 +1,277 @@
+/*
+ * zero_oracle.c -- plain, slow, sequential CPU oracle for the per-rank
+ * ZeRO-1 shard step of mixed-precision data-parallel training.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load or call this code. The HIP library
+ * never includes, links or calls it, and it shares no source with that
+ * library (no headers, helpers, tables or constants).
+ *
+ * Pages cited below:
+ *   [ZeRO ch.]  "第2章 软件程序与专用硬件的结合" (zhurongshuo.com), section
+ *               2.3.4 "ZeRO：数据并行的革命性优化", Stage 1 paragraph.
+ *   [CS336 L7]  "CS336 Lecture 7: Parallelism 1" (hqhq1025.github.io),
+ *               sections "五种基本集合通信操作" (collective primitives),
+ *               "核心恒等式" (All-Reduce = Reduce-Scatter + All-Gather),
+ *               "训练内存的详细分析" (the 16-bytes-per-parameter table), and
+ *               "ZeRO Stage 1：优化器状态分片" (the four-step workflow).
+ *   [5D post]   gsyq.cn/news/457874, section 3.2 trap 3 (AMP gradient
+ *               scaling, loss going to inf) and section 4.2 (the
+ *               deepspeed_config.json optimizer block: AdamW with lr, betas,
+ *               eps, weight_decay; the fp16 loss-scale block).
+ *
+ * What one step computes, in this order ([CS336 L7] ZeRO Stage 1 workflow:
+ * reduce-scatter the gradients, update the local shard, all-gather the
+ * parameters):
+ *
+ *   1. reduce    s[i] = fold over ranks r = 0..M-1, ascending, of the bf16
+ *                gradient replicas converted to binary32, starting from the
+ *                rank-0 value; every add is one binary32 add rounded to
+ *                nearest even. GPU i receives the *summed* gradient of its
+ *                shard ([CS336 L7] Stage 1 step 2, Reduce-Scatter).
+ *   2. unscale   g[i] = s[i] * scale32, scale32 = the scale rounded once to
+ *                binary32 (AMP: the gradient is multiplied by 1/S after the
+ *                sum; [5D post] 3.2 trap 3).
+ *   3. check     found_inf = any g[i] not finite; sumsq = sum of g[i]^2 in
+ *                binary64, in index order.
+ *   4. finalize  norm = sqrt(sumsq + external_sumsq);
+ *                coef = min(1, max_norm / (norm + 1e-6)) when max_norm > 0,
+ *                else 1 (NaN propagates); skip = found_inf && skip_on_nonfinite.
+ *                Clipping by the global L2 norm is not described on the pages;
+ *                this is the common framework convention, read as such.
+ *   5. update    (only when not skipped; a skipped step writes nothing)
+ *                AdamW with bias correction, eps outside the square root and
+ *                weight decay decoupled from the gradient and scaled by lr
+ *                ([5D post] 4.2 names the optimizer "AdamW" and its knobs;
+ *                [CS336 L7] memory table: fp32 master, fp32 first and second
+ *                moments). Evaluated in binary64 from the binary32 state and
+ *                rounded once to binary32 on store.
+ *   6. emit      out[i] = bf16 round-to-nearest-even of the new binary32
+ *                master value (the shard the all-gather would broadcast;
+ *                [CS336 L7] Stage 1 step 4).
+ *
+ * Compile with -O2 -ffp-contract=off and without -ffast-math: the binary32
+ * fold of step 1 must be exactly the sequence of rounded adds written here.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bf16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.           */
+/* ------------------------------------------------------------------------ */
+
+/* Value of one bf16 bit pattern, read from its fields. */
+static float bf16_value_from_fields(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 7) & 0xFF;
+    const int f = h & 0x7F;
+    double mag;
+    if (e == 0xFF) {
+        if (f != 0) return sign ? -NAN : NAN;
+        return sign ? -INFINITY : INFINITY;
+    }
+    if (e == 0)
+        mag = ldexp((double)f, -126 - 7);           /* 0.f x 2^-126 */
+    else
+        mag = ldexp((double)(128 + f), e - 127 - 7); /* 1.f x 2^(e-127) */
+    return (float)(sign ? -mag : mag);               /* exact in binary32 */
+}
+
+static float g_bf16_table[65536];
+static int g_bf16_table_ready = 0;
+
+static void bf16_table_init(void)
+{
+    if (g_bf16_table_ready) return;
+    for (uint32_t h = 0; h < 65536u; ++h) g_bf16_table[h] = bf16_value_from_fields((uint16_t)h);
+    g_bf16_table_ready = 1;
+}
+
+static inline float bf16_to_float(uint16_t h) { return g_bf16_table[h]; }
+
+/* Largest finite bf16: (2 - 2^-7) * 2^127 = 255 * 2^120. */
+#define BF16_MAX_FINITE (255.0 * 0x1p120)
+
+/* Encode a value that is already exactly representable in bf16. */
+static uint16_t bf16_encode_exact(double r, uint16_t s)
+{
+    int e;
+    if (r == 0.0) return s;
+    frexp(r, &e); /* r = f * 2^e, 0.5 <= f < 1: unbiased exponent e-1 */
+    if (e - 1 >= -126) {
+        const int frac = (int)ldexp(r, -(e - 1 - 7)) - 128;
+        return (uint16_t)(s | ((e - 1 + 127) << 7) | frac);
+    }
+    return (uint16_t)(s | (int)ldexp(r, 126 + 7));
+}
+
+/* Round a binary32 value to bf16, to nearest, ties to even (IEEE 754). */
+static uint16_t bf16_round_nearest_even(float x)
+{
+    if (isnan(x)) return signbit(x) ? 0xFFC0 : 0x7FC0; /* quiet NaN, sign kept */
+    const uint16_t s = signbit(x) ? 0x8000 : 0;
+    if (isinf(x)) return (uint16_t)(s | 0x7F80);
+    const double a = fabs((double)x);
+    if (a == 0.0) return s;
+    int e;
+    frexp(a, &e);
+    /* exponent of the last bit bf16 keeps: 7 fraction bits below the leading
+     * bit for normals, fixed at 2^-133 for subnormals */
+    const int q = (e - 1 >= -126) ? (e - 1 - 7) : (-126 - 7);
+    const double k = nearbyint(ldexp(a, -q)); /* ties to even */
+    const double r = ldexp(k, q);
+    if (r > BF16_MAX_FINITE) return (uint16_t)(s | 0x7F80);
+    return bf16_encode_exact(r, s);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exported helpers for the pins.                                           */
+/* ------------------------------------------------------------------------ */
+
+void oracle_bf16_to_f32(const uint16_t* in, float* out, int64_t n)
+{
+    bf16_table_init();
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_float(in[i]);
+}
+
+void oracle_f32_to_bf16(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round_nearest_even(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 1 + 2: reduce the M replicas of one shard, then unscale.            */
+/* ------------------------------------------------------------------------ */
+
+void oracle_reduce(const uint16_t* const* grads, int32_t M, int64_t n, double grad_scale, float* g_out)
+{
+    bf16_table_init();
+    const float scale = (float)grad_scale;
+    for (int64_t i = 0; i < n; ++i) {
+        float s = bf16_to_float(grads[0][i]);
+        for (int32_t r = 1; r < M; ++r) s = s + bf16_to_float(grads[r][i]);
+        g_out[i] = s * scale;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 3: non-finite flag and sum of squares. The accumulators are in/out  */
+/* so that consecutive slices chain in index order.                         */
+/* ------------------------------------------------------------------------ */
+
+void oracle_check(const float* g, int64_t n, double* sumsq, int32_t* found_inf)
+{
+    double acc = *sumsq;
+    int32_t bad = *found_inf;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(g[i])) bad = 1;
+        acc += (double)g[i] * (double)g[i];
+    }
+    *sumsq = acc;
+    *found_inf = bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 4: norm, clip coefficient, skip decision.                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    double sumsq;     /* local sum of squares plus external_sumsq */
+    double grad_norm; /* sqrt(sumsq) */
+    double clip_coef; /* multiplier applied to g before the update */
+    int32_t found_inf;
+    int32_t skipped;
+} oracle_result;
+
+void oracle_finalize(double sumsq, double external_sumsq, int32_t found_inf, double max_grad_norm,
+                     int32_t skip_on_nonfinite, oracle_result* res)
+{
+    const double total = sumsq + external_sumsq;
+    const double norm = sqrt(total);
+    double coef = 1.0;
+    if (max_grad_norm > 0.0) {
+        coef = max_grad_norm / (norm + 1e-6);
+        if (coef > 1.0) coef = 1.0; /* a NaN coefficient stays NaN */
+    }
+    res->sumsq = total;
+    res->grad_norm = norm;
+    res->clip_coef = coef;
+    res->found_inf = found_inf ? 1 : 0;
+    res->skipped = (found_inf && skip_on_nonfinite) ? 1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 5 + 6: AdamW on the fp32 master, m, v, then the bf16 emit.          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;         /* t >= 1: the index of this update */
+    double max_grad_norm; /* <= 0: no clipping */
+    double grad_scale;    /* multiplies the fp32 sum */
+    int32_t skip_on_nonfinite;
+} oracle_hparams;
+
+void oracle_adamw(float* master, float* exp_avg, float* exp_avg_sq, const float* g, uint16_t* out, int64_t n,
+                  const oracle_hparams* hp, double coef)
+{
+    const double t = (double)hp->step;
+    const double bc1 = 1.0 - pow(hp->beta1, t); /* bias corrections of m and v */
+    const double bc2 = 1.0 - pow(hp->beta2, t);
+    for (int64_t i = 0; i < n; ++i) {
+        const double gi = (double)g[i] * coef;
+        const double m = hp->beta1 * (double)exp_avg[i] + (1.0 - hp->beta1) * gi;
+        const double v = hp->beta2 * (double)exp_avg_sq[i] + (1.0 - hp->beta2) * gi * gi;
+        const double m_hat = m / bc1;
+        const double v_hat = v / bc2;
+        const double theta = (double)master[i] * (1.0 - hp->lr * hp->weight_decay)
+                             - hp->lr * m_hat / (sqrt(v_hat) + hp->eps);
+        exp_avg[i] = (float)m;
+        exp_avg_sq[i] = (float)v;
+        master[i] = (float)theta;
+        out[i] = bf16_round_nearest_even(master[i]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The whole step over a list of tensors (one shard each).                  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int64_t n;
+    const uint16_t* const* grads; /* M pointers, n bf16 values each */
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    uint16_t* param_out; /* n bf16 values */
+} oracle_tensor;
+
+/* Returns 0, or -1 when scratch memory cannot be had. */
+int32_t oracle_zero_step(const oracle_tensor* ts, int32_t T, int32_t M, const oracle_hparams* hp,
+                         double external_sumsq, oracle_result* res)
+{
+    float** gs = (float**)calloc((size_t)(T > 0 ? T : 1), sizeof(float*));
+    if (!gs) return -1;
+    double sumsq = 0.0;
+    int32_t found_inf = 0;
+    int32_t rc = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        gs[t] = (float*)malloc((size_t)(ts[t].n > 0 ? ts[t].n : 1) * sizeof(float));
+        if (!gs[t]) { rc = -1; goto done; }
+        oracle_reduce(ts[t].grads, M, ts[t].n, hp->grad_scale, gs[t]);
+        oracle_check(gs[t], ts[t].n, &sumsq, &found_inf);
+    }
+    oracle_finalize(sumsq, external_sumsq, found_inf, hp->max_grad_norm, hp->skip_on_nonfinite, res);
+    if (!res->skipped)
+        for (int32_t t = 0; t < T; ++t)
+            oracle_adamw(ts[t].master, ts[t].exp_avg, ts[t].exp_avg_sq, gs[t], ts[t].param_out, ts[t].n, hp,
+                         res->clip_coef);
+done:
+    for (int32_t t = 0; t < T; ++t) free(gs[t]);
+    free(gs);
+    return rc;
+}
