@@ -1,0 +1,197 @@
+/*
+ * zero_step.h -- C ABI of the fused per-rank ZeRO-1 shard step for MI355X
+ * (gfx950).
+ *
+ * The operation ("CS336 Lecture 7: Parallelism 1", section "ZeRO Stage 1：
+ * 优化器状态分片", the four-step workflow; "第2章 软件程序与专用硬件的结合",
+ * section 2.3.4, Stage 1): every data-parallel rank holds a full bf16
+ * gradient; a reduce-scatter gives rank i the *sum* over ranks of shard i;
+ * rank i updates shard i with the optimizer state it alone keeps (fp32
+ * master weights, fp32 first and second moments: the 16-bytes-per-parameter
+ * table of section "训练内存的详细分析"); an all-gather then broadcasts the
+ * updated bf16 parameters. This library performs the part of that step that
+ * runs at one rank, on one GPU: the M gradient replicas of the shard are M
+ * buffers in this GPU's memory.
+ *
+ *   g[i]  = (((g_0[i] + g_1[i]) + g_2[i]) + ... + g_{M-1}[i]) * grad_scale
+ *           in binary32, ranks in ascending order, from the rank-0 value;
+ *   found_inf = any g[i] is inf or NaN;
+ *   norm  = sqrt(sum of g[i]^2 + external_sumsq)        (binary64 partials)
+ *   coef  = min(1, max_grad_norm / (norm + 1e-6)) if max_grad_norm > 0 else 1
+ *   skip  = found_inf && skip_on_nonfinite      (a skipped step writes nothing)
+ *   AdamW (bias-corrected, eps outside the root, decay scaled by lr):
+ *     m   = b1*m + (1-b1)*(coef*g);   v = b2*v + (1-b2)*(coef*g)^2
+ *     w   = w*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps)
+ *   out   = bf16 round-to-nearest-even of the new fp32 w (the all-gather payload)
+ *
+ * AMP unscaling (grad_scale = 1/S) and the inf/NaN skip follow the
+ * loss-scaling behaviour described in gsyq.cn/news/457874, section 3.2 trap 3;
+ * the AdamW knob names follow its section 4.2 optimizer block. Clipping by the
+ * global L2 norm is not on the pages; the coefficient is the common framework
+ * convention above.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev, and every tensor pointer, are device pointers on the
+ *    current HIP device. Arrays of pointers (grads) are HOST arrays holding
+ *    device pointers. Structs passed by pointer (hparams, tensors) are host
+ *    memory, read during the call only.
+ *  - bf16 data are raw 16-bit codes (uint16). fp32 data are IEEE binary32.
+ *  - The caller owns all memory. The library allocates no device memory; it
+ *    keeps a small host-side cache of workspace plans.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and returns
+ *    after enqueueing. Results are device-resident.
+ *  - Errors: an int status (ZERO_OK or ZERO_ERR_*). On any error nothing is
+ *    launched and no memory is written. n == 0 is a valid no-op. No C++
+ *    exception crosses the ABI.
+ *  - Any alignment is accepted; when all pointers of a tensor share their
+ *    alignment modulo 16 bytes the kernels use 16-byte vector accesses.
+ *  - Outputs must not alias inputs, except the in-place master/exp_avg/
+ *    exp_avg_sq. The library never advances `step`: the caller increments it
+ *    when the result record says `skipped == 0`.
+ */
+#ifndef ZERO_STEP_H
+#define ZERO_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ZERO_OK 0
+#define ZERO_ERR_INVALID_ARGUMENT 1    /* null pointer, bad size or hyperparameter */
+#define ZERO_ERR_WORKSPACE_TOO_SMALL 2 /* ws_bytes below the size query's answer */
+#define ZERO_ERR_HIP 3                 /* a HIP runtime call failed (launch, copy) */
+#define ZERO_ERR_STALE_WORKSPACE 4     /* set in zero_result.status by the device when a
+                                          workspace no longer holds the plan of this call;
+                                          the step then wrote nothing */
+
+/* Largest M accepted (ranks, i.e. gradient replicas per shard). */
+#define ZERO_MAX_RANKS 65536
+
+/* AdamW hyperparameters of one step (names as in a deepspeed_config.json
+ * optimizer block, gsyq.cn/news/457874 section 4.2). Host memory. */
+typedef struct zero_adamw_hparams {
+    double lr;                 /* learning rate, finite, >= 0 */
+    double beta1;              /* first-moment decay, in [0, 1) */
+    double beta2;              /* second-moment decay, in [0, 1) */
+    double eps;                /* added to sqrt of the bias-corrected v, finite, >= 0 */
+    double weight_decay;       /* decoupled: w *= (1 - lr*weight_decay); finite */
+    int64_t step;              /* t >= 1: index of this update (bias corrections) */
+    double max_grad_norm;      /* > 0: clip g to this global L2 norm; <= 0: off */
+    double grad_scale;         /* multiplies the fp32 sum, rounded to fp32 once: 1,
+                                  1/S for an AMP loss scale S, 1/M for a mean; finite, > 0 */
+    int32_t skip_on_nonfinite; /* nonzero: any inf/NaN in g skips the whole update */
+    int32_t reserved;          /* must be 0 */
+} zero_adamw_hparams;
+
+/* One tensor's shard in a zero_step bucket list. Host memory. */
+typedef struct zero_tensor {
+    int64_t n;                /* elements in this shard, >= 0 */
+    const void* const* grads; /* HOST array of M device pointers, n bf16 each (read only) */
+    float* master;            /* device, n fp32 master weights, updated in place */
+    float* exp_avg;           /* device, n fp32 first moments, updated in place */
+    float* exp_avg_sq;        /* device, n fp32 second moments, updated in place */
+    void* param_out;          /* device, n bf16 codes, written (the all-gather payload) */
+} zero_tensor;
+
+/* Device-resident result record of a step, 32 bytes, written by the library. */
+typedef struct zero_result {
+    double sumsq;      /* sum of g^2 over every element of the call, plus external_sumsq */
+    float grad_norm;   /* sqrt(sumsq) rounded to fp32 (inf/NaN when found_inf) */
+    float clip_coef;   /* coefficient applied to g (1 when clipping is off) */
+    int32_t found_inf; /* 1 when any unscaled reduced gradient is inf or NaN */
+    int32_t skipped;   /* 1 when the update was not applied */
+    int32_t status;    /* ZERO_OK, or ZERO_ERR_STALE_WORKSPACE */
+    int32_t reserved;
+} zero_result;
+
+/*
+ * zero_shard_reduce -- the reduce-scatter arithmetic at one rank
+ * ("CS336 Lecture 7", section "五种基本集合通信操作", Reduce-Scatter; section
+ * "ZeRO Stage 1", step 2: GPU i receives the summed gradient of shard i).
+ *   g_out[i] = fl32(fold_{r=0..M-1} bf16->fp32(grads[r][i])) * fl32(grad_scale)
+ * grads: host array of M device pointers to n bf16 codes. g_out: device, n
+ * fp32, must not overlap any replica. 1 <= M <= ZERO_MAX_RANKS, n >= 0,
+ * grad_scale finite and > 0. Bit-exact: the fold order is fixed.
+ */
+int zero_shard_reduce(const void* const* grads, int32_t M, int64_t n, double grad_scale, float* g_out,
+                      hipStream_t stream);
+
+/*
+ * zero_grad_check_norm_workspace_bytes -- workspace size for
+ * zero_grad_check_norm over n elements (0 when n == 0).
+ */
+size_t zero_grad_check_norm_workspace_bytes(int64_t n);
+
+/*
+ * zero_grad_check_norm -- non-finite check, global L2 norm, clip coefficient
+ * and skip decision over an fp32 gradient g (device, n elements), written to
+ * the device record res_dev. hp may be NULL (no clipping, no skip); only its
+ * max_grad_norm and skip_on_nonfinite are read. external_sumsq (>= 0 or NaN/inf
+ * propagates) is the other ranks' sum of squares for a multi-GPU caller; 0 on
+ * one GPU. ws: device workspace of at least
+ * zero_grad_check_norm_workspace_bytes(n) bytes, contents irrelevant on entry.
+ * The sum of squares uses exact binary64 squares and a fixed reduction tree
+ * (bitwise repeatable on one device).
+ */
+int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp, double external_sumsq,
+                         void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
+
+/*
+ * zero_adamw_step -- AdamW on fp32 master/exp_avg/exp_avg_sq (device, n each,
+ * in place) from the fp32 gradient g (device, n), plus the bf16 emit into
+ * param_out (device, n bf16 codes). hp is required (max_grad_norm and
+ * skip_on_nonfinite are ignored here). res_dev (device, may be NULL) supplies
+ * clip_coef and skipped from zero_grad_check_norm: when skipped is set the
+ * kernel writes nothing; when res_dev is NULL the coefficient is 1.
+ */
+int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out, int64_t n,
+                    const zero_adamw_hparams* hp, const zero_result* res_dev, hipStream_t stream);
+
+/*
+ * zero_step_workspace_bytes -- workspace size for zero_step over this tensor
+ * list and hyperparameters (pointers inside `tensors` are not read). Returns 0
+ * on invalid arguments.
+ */
+size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp);
+
+/*
+ * zero_step -- the fused step over a bucket list of T tensor shards, each with
+ * M bf16 replicas ("CS336 Lecture 7", "ZeRO Stage 1" steps 2-3 and the
+ * payload of step 4; per-layer buckets as in its section "ZeRO Stage 2").
+ * The norm and found_inf are global over all T tensors. Without clipping and
+ * skipping it is one streaming pass; with either, a first pass writes the fp32
+ * reduced gradient to the workspace and a second pass applies the update.
+ * ws: device workspace of zero_step_workspace_bytes(...) bytes, 256-byte
+ * aligned. The workspace caches the tensor table of the call; it belongs to
+ * the library from this call until the caller reuses it for anything else,
+ * and two calls that share a workspace must not run concurrently. res_dev:
+ * device result record. Returns ZERO_ERR_WORKSPACE_TOO_SMALL if ws_bytes is
+ * short.
+ */
+int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+              double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
+
+/*
+ * zero_workspace_forget -- drop the host-side record that `ws` holds the
+ * tensor table of an earlier zero_step call. Call it before freeing or
+ * repurposing such a workspace; the next zero_step on it then rewrites the
+ * table. (A workspace whose table was overwritten without this call is
+ * detected on the device: zero_result.status = ZERO_ERR_STALE_WORKSPACE and
+ * nothing is written.) Host only; launches nothing.
+ */
+int zero_workspace_forget(const void* ws);
+
+/* Human-readable text of a status code (static storage). */
+const char* zero_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_STEP_H */

@@ -1,0 +1,272 @@
+"""Fused per-rank ZeRO-1 shard step for MI355X (gfx950): a thin ctypes binding
+of the C ABI declared in ``include/zero_step.h``.
+
+This module only marshals arguments (torch tensors -> device pointers and the
+current HIP stream). Every step of the computation runs in the HIP kernels of
+``libzero_step.so``; there is no CPU fallback: if the library is missing the
+first call raises.
+
+Functions keep the C names:
+
+* ``zero_shard_reduce(grads, grad_scale, g_out)``
+* ``zero_grad_check_norm_workspace_bytes(n)``
+* ``zero_grad_check_norm(g, hp, external_sumsq, ws, res)``
+* ``zero_adamw_step(master, exp_avg, exp_avg_sq, g, param_out, hp, res=None)``
+* ``zero_step_workspace_bytes(tensors, M, hp)``
+* ``zero_step(tensors, hp, external_sumsq, ws, res)``
+* ``zero_workspace_forget(ws)``, ``zero_status_string(status)``
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import struct
+import weakref
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_step.so")
+
+ZERO_OK = 0
+ZERO_ERR_INVALID_ARGUMENT = 1
+ZERO_ERR_WORKSPACE_TOO_SMALL = 2
+ZERO_ERR_HIP = 3
+ZERO_ERR_STALE_WORKSPACE = 4
+RESULT_BYTES = 32
+
+# Every symbol the C ABI exports (include/zero_step.h).
+EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_grad_check_norm", "zero_adamw_step",
+           "zero_step_workspace_bytes", "zero_step", "zero_workspace_forget", "zero_status_string")
+
+
+class _CHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64),
+                ("max_grad_norm", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("skip_on_nonfinite", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _CTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {zero_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, dbl, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
+        L.zero_shard_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, dbl, vp, vp]
+        L.zero_shard_reduce.restype = ctypes.c_int
+        L.zero_grad_check_norm_workspace_bytes.argtypes = [i64]
+        L.zero_grad_check_norm_workspace_bytes.restype = sz
+        L.zero_grad_check_norm.argtypes = [vp, i64, ctypes.POINTER(_CHparams), dbl, vp, sz, vp, vp]
+        L.zero_grad_check_norm.restype = ctypes.c_int
+        L.zero_adamw_step.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_CHparams), vp, vp]
+        L.zero_adamw_step.restype = ctypes.c_int
+        L.zero_step_workspace_bytes.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams)]
+        L.zero_step_workspace_bytes.restype = sz
+        L.zero_step.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams), dbl, vp, sz, vp, vp]
+        L.zero_step.restype = ctypes.c_int
+        L.zero_workspace_forget.argtypes = [vp]
+        L.zero_workspace_forget.restype = ctypes.c_int
+        L.zero_status_string.argtypes = [ctypes.c_int]
+        L.zero_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+@dataclasses.dataclass
+class HParams:
+    """AdamW knobs of one step (names of a deepspeed_config.json optimizer
+    block), the step index t >= 1, the clip threshold (<= 0: off), the
+    multiplier of the fp32 gradient sum, and the skip switch."""
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+    step: int = 1
+    max_grad_norm: float = 0.0
+    grad_scale: float = 1.0
+    skip_on_nonfinite: int = 0
+
+    def _c(self) -> _CHparams:
+        return _CHparams(float(self.lr), float(self.beta1), float(self.beta2), float(self.eps),
+                         float(self.weight_decay), int(self.step), float(self.max_grad_norm), float(self.grad_scale),
+                         int(bool(self.skip_on_nonfinite)), 0)
+
+
+@dataclasses.dataclass
+class ZeroTensor:
+    """One tensor's shard: M bf16 gradient replicas, fp32 master/exp_avg/
+    exp_avg_sq (updated in place) and the bf16 output shard."""
+    grads: List[torch.Tensor]
+    master: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    param_out: torch.Tensor
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str, n: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+
+
+def _check(status: int, where: str):
+    if status != ZERO_OK:
+        raise ZeroError(status, where)
+
+
+def zero_status_string(status: int) -> str:
+    return lib().zero_status_string(int(status)).decode()
+
+
+def new_result(device=None) -> torch.Tensor:
+    """A 32-byte device buffer for the zero_result record."""
+    return torch.zeros(RESULT_BYTES, dtype=torch.uint8, device=device or "cuda")
+
+
+def read_result(res: torch.Tensor) -> dict:
+    """Copy the record to the host (synchronizes with its stream)."""
+    b = bytes(res.cpu().numpy().tobytes())
+    sumsq, norm, coef, found_inf, skipped, status, _ = struct.unpack("<dffiiii", b)
+    return dict(sumsq=sumsq, grad_norm=norm, clip_coef=coef, found_inf=found_inf, skipped=skipped, status=status)
+
+
+def zero_shard_reduce(grads: Sequence[torch.Tensor], grad_scale: float, g_out: torch.Tensor, stream=None) -> None:
+    n = g_out.numel()
+    _need(g_out, torch.float32, "g_out")
+    for r, g in enumerate(grads):
+        _need(g, torch.bfloat16, f"grads[{r}]", n)
+    arr = (ctypes.c_void_p * max(len(grads), 1))(*[g.data_ptr() for g in grads])
+    _check(lib().zero_shard_reduce(arr, len(grads), n, float(grad_scale), g_out.data_ptr(), _stream(stream)),
+           "zero_shard_reduce")
+
+
+def zero_grad_check_norm_workspace_bytes(n: int) -> int:
+    return int(lib().zero_grad_check_norm_workspace_bytes(int(n)))
+
+
+def zero_grad_check_norm(g: torch.Tensor, hp: Optional[HParams], external_sumsq: float, ws: Optional[torch.Tensor],
+                         res: torch.Tensor, stream=None) -> None:
+    _need(g, torch.float32, "g")
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    h = hp._c() if hp is not None else None
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_grad_check_norm(g.data_ptr(), g.numel(), ctypes.byref(h) if h is not None else None,
+                                      float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
+           "zero_grad_check_norm")
+
+
+def zero_adamw_step(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, g: torch.Tensor,
+                    param_out: torch.Tensor, hp: HParams, res: Optional[torch.Tensor] = None, stream=None) -> None:
+    n = master.numel()
+    for t, nm in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (g, "g")):
+        _need(t, torch.float32, nm, n)
+    _need(param_out, torch.bfloat16, "param_out", n)
+    if res is not None:
+        _need(res, torch.uint8, "res", RESULT_BYTES)
+    h = hp._c()
+    _check(lib().zero_adamw_step(master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), g.data_ptr(),
+                                 param_out.data_ptr(), n, ctypes.byref(h), _ptr(res), _stream(stream)),
+           "zero_adamw_step")
+
+
+def _ctensors(tensors: Sequence[ZeroTensor], check: bool):
+    M = len(tensors[0].grads) if tensors else 1
+    keep = []
+    arr = (_CTensor * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        n = t.master.numel()
+        if check:
+            if len(t.grads) != M:
+                raise ValueError(f"tensor {i}: {len(t.grads)} replicas, expected {M}")
+            for r, g in enumerate(t.grads):
+                _need(g, torch.bfloat16, f"tensors[{i}].grads[{r}]", n)
+            for x, nm in ((t.master, "master"), (t.exp_avg, "exp_avg"), (t.exp_avg_sq, "exp_avg_sq")):
+                _need(x, torch.float32, f"tensors[{i}].{nm}", n)
+            _need(t.param_out, torch.bfloat16, f"tensors[{i}].param_out", n)
+        ptrs = (ctypes.c_void_p * max(M, 1))(*[g.data_ptr() for g in t.grads])
+        keep.append(ptrs)
+        arr[i] = _CTensor(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), t.master.data_ptr(),
+                          t.exp_avg.data_ptr(), t.exp_avg_sq.data_ptr(), t.param_out.data_ptr())
+    return arr, keep, M
+
+
+def zero_step_workspace_bytes(tensors: Sequence[ZeroTensor], M: int, hp: HParams) -> int:
+    arr, keep, _ = _ctensors(tensors, check=False)
+    h = hp._c()
+    return int(lib().zero_step_workspace_bytes(arr, len(tensors), int(M), ctypes.byref(h)))
+
+
+def zero_step(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float, ws: Optional[torch.Tensor],
+              res: torch.Tensor, stream=None) -> None:
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    arr, keep, M = _ctensors(tensors, check=True)
+    h = hp._c()
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), _ptr(ws), wsb,
+                           res.data_ptr(), _stream(stream)), "zero_step")
+
+
+def zero_workspace_forget(ws: torch.Tensor) -> None:
+    _check(lib().zero_workspace_forget(ws.data_ptr()), "zero_workspace_forget")
+
+
+def workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
+    """A device workspace of nbytes (torch allocations are 256-byte aligned).
+    When the tensor is freed, the library forgets any plan it cached there:
+    the allocator may hand the same memory out again for something else."""
+    if nbytes <= 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+    weakref.finalize(ws, _forget_ptr, ws.data_ptr())
+    return ws
+
+
+def _forget_ptr(ptr: int) -> None:
+    if _lib is not None:
+        _lib.zero_workspace_forget(ptr)
+
+
+def zero_step_workspace_bytes_for_sizes(sizes: Sequence[int], M: int, hp: HParams) -> int:
+    """Workspace size of a zero_step over shards of these lengths (no tensors needed)."""
+    arr = (_CTensor * max(len(sizes), 1))()
+    for i, n in enumerate(sizes):
+        arr[i] = _CTensor(int(n), None, None, None, None, None)
+    h = hp._c()
+    return int(lib().zero_step_workspace_bytes(arr, len(sizes), int(M), ctypes.byref(h)))

@@ -1,0 +1,369 @@
+// zero_api.cpp -- the C ABI of the fused ZeRO-1 shard step: argument checks,
+// host-side scalar derivation, element layouts, the zero_step workspace plan
+// and the launch sequence. Every kernel is in zero_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "zero_internal.h"
+#include "zero_step.h"
+
+using namespace zero;
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool is_fin(double x) { return std::isfinite(x); }
+
+bool hparams_ok(const zero_adamw_hparams* hp)
+{
+    if (hp == nullptr) return false;
+    if (!is_fin(hp->lr) || hp->lr < 0.0) return false;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return false;
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return false;
+    if (!is_fin(hp->eps) || hp->eps < 0.0) return false;
+    if (!is_fin(hp->weight_decay)) return false;
+    if (hp->step < 1) return false;
+    if (std::isnan(hp->max_grad_norm)) return false;
+    if (!is_fin(hp->grad_scale) || !(hp->grad_scale > 0.0)) return false;
+    if (hp->reserved != 0) return false;
+    return true;
+}
+
+// The fp32 scalars of one step, from binary64 ("CS336 Lecture 7", memory
+// table: the update runs on fp32 master, m and v).
+AdamScalars derive(const zero_adamw_hparams* hp)
+{
+    const double t = static_cast<double>(hp->step);
+    const double bc1 = 1.0 - std::pow(hp->beta1, t);
+    const double bc2 = 1.0 - std::pow(hp->beta2, t);
+    AdamScalars c;
+    c.b1 = static_cast<float>(hp->beta1);
+    c.omb1 = static_cast<float>(1.0 - hp->beta1);
+    c.b2 = static_cast<float>(hp->beta2);
+    c.omb2 = static_cast<float>(1.0 - hp->beta2);
+    c.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+    c.step_size = static_cast<float>(hp->lr / bc1);
+    c.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+    c.eps = static_cast<float>(hp->eps);
+    return c;
+}
+
+bool two_pass_of(const zero_adamw_hparams* hp) { return hp->max_grad_norm > 0.0 || hp->skip_on_nonfinite != 0; }
+
+// Vector mode needs one head length h in [0, 8) at which every bf16 pointer
+// (2-byte elements) and every fp32 pointer (4-byte elements) is 16-byte
+// aligned; otherwise the shard is visited element by element.
+Layout make_layout(int64_t n, const std::vector<uintptr_t>& b16, const std::vector<uintptr_t>& f32)
+{
+    Layout L{n, -1, 0, 0};
+    if (n <= 0) return L;
+    for (int h = 0; h < kVec; ++h) {
+        bool ok = true;
+        for (uintptr_t p : b16)
+            if ((p + 2u * h) % 16u != 0) { ok = false; break; }
+        if (ok)
+            for (uintptr_t p : f32)
+                if ((p + 4u * h) % 16u != 0) { ok = false; break; }
+        if (!ok) continue;
+        if (h > n) break;
+        L.head = h;
+        L.nvec = (n - h) / kVec;
+        L.tail = static_cast<int32_t>(n - h - kVec * L.nvec);
+        return L;
+    }
+    return L;
+}
+
+int grid_for(int64_t tiles, int resident)
+{
+    if (tiles <= 0) return 1;
+    return static_cast<int>(tiles < resident ? tiles : resident);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
+
+// ------------------------------------------------------------------ plans
+
+PlanOffsets plan_offsets(const zero_tensor* ts, int32_t T, int32_t M, bool two_pass)
+{
+    PlanOffsets o{};
+    int64_t tiles = 0;
+    size_t gbytes = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        tiles += tiles_bound(ts[t].n);
+        if (two_pass && ts[t].n > 0) gbytes += align_up((static_cast<size_t>(ts[t].n) + 3) * 4, kAlign);
+    }
+    o.desc = kAlign;
+    o.ptrs = align_up(o.desc + sizeof(TensorDesc) * static_cast<size_t>(T), kAlign);
+    o.tiles = align_up(o.ptrs + sizeof(void*) * static_cast<size_t>(T) * static_cast<size_t>(M), kAlign);
+    o.parts = align_up(o.tiles + sizeof(TileRef) * static_cast<size_t>(tiles), kAlign);
+    o.gbuf = align_up(o.parts + sizeof(Partial) * static_cast<size_t>(kMaxPartials), kAlign);
+    o.total = o.gbuf + gbytes;
+    return o;
+}
+
+uint64_t fnv1a(const uint8_t* p, size_t n, uint64_t h)
+{
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+std::mutex g_plan_mu;
+std::map<std::pair<int, uintptr_t>, uint64_t> g_plan_cache;  // (device, ws) -> signature held there
+
+void forget_ws(const void* ws)
+{
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    for (auto it = g_plan_cache.begin(); it != g_plan_cache.end();) {
+        if (it->first.second == reinterpret_cast<uintptr_t>(ws)) it = g_plan_cache.erase(it);
+        else ++it;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_status_string(int status)
+{
+    switch (status) {
+    case ZERO_OK: return "ok";
+    case ZERO_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ZERO_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ZERO_ERR_HIP: return "HIP runtime error";
+    case ZERO_ERR_STALE_WORKSPACE: return "workspace no longer holds the plan of this call";
+    default: return "unknown status";
+    }
+}
+
+int zero_shard_reduce(const void* const* grads, int32_t M, int64_t n, double grad_scale, float* g_out,
+                      hipStream_t stream)
+{
+    if (n < 0 || M < 1 || M > ZERO_MAX_RANKS) return ZERO_ERR_INVALID_ARGUMENT;
+    if (!is_fin(grad_scale) || !(grad_scale > 0.0)) return ZERO_ERR_INVALID_ARGUMENT;
+    if (n == 0) return ZERO_OK;
+    if (grads == nullptr || g_out == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    std::vector<uintptr_t> b16;
+    b16.reserve(M);
+    for (int32_t r = 0; r < M; ++r) {
+        if (grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        b16.push_back(reinterpret_cast<uintptr_t>(grads[r]));
+    }
+    const Layout L = make_layout(n, b16, {reinterpret_cast<uintptr_t>(g_out)});
+    const float scale = static_cast<float>(grad_scale);
+    const int64_t tiles = layout_tiles(L);
+    for (int32_t r0 = 0; r0 < M; r0 += kInlineRanks) {
+        const int Mc = (M - r0) < kInlineRanks ? (M - r0) : kInlineRanks;
+        RankPtrs p{};
+        for (int j = 0; j < Mc; ++j) p.p[j] = static_cast<const uint16_t*>(grads[r0 + j]);
+        const bool first = r0 == 0, last = r0 + Mc == M;
+        const int grid = grid_for(tiles, resident_grid_reduce(Mc, first));
+        const hipError_t e = launch_reduce(p, Mc, first, last, scale, L, g_out, grid, stream);
+        if (e != hipSuccess) return ZERO_ERR_HIP;
+    }
+    return ZERO_OK;
+}
+
+size_t zero_grad_check_norm_workspace_bytes(int64_t n)
+{
+    return n > 0 ? sizeof(Partial) * static_cast<size_t>(kMaxPartials) : 0;
+}
+
+int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp, double external_sumsq, void* ws,
+                         size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
+{
+    if (n < 0 || res_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    if (hp != nullptr && !hparams_ok(hp)) return ZERO_ERR_INVALID_ARGUMENT;
+    const double max_norm = hp ? hp->max_grad_norm : 0.0;
+    const int skip = hp ? (hp->skip_on_nonfinite != 0) : 0;
+    if (n == 0)
+        return hip_status(launch_finalize(nullptr, 0, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+    if (g == nullptr || ws == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    if (reinterpret_cast<uintptr_t>(ws) % 16u != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < zero_grad_check_norm_workspace_bytes(n)) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+    forget_ws(ws);  // a zero_step plan cached in this workspace is overwritten
+    const Layout L = make_layout(n, {}, {reinterpret_cast<uintptr_t>(g)});
+    const int grid = grid_for(layout_tiles(L), resident_grid_check());
+    Partial* parts = static_cast<Partial*>(ws);
+    hipError_t e = launch_check(g, L, parts, grid, stream);
+    if (e != hipSuccess) return ZERO_ERR_HIP;
+    return hip_status(launch_finalize(parts, grid, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+}
+
+int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out, int64_t n,
+                    const zero_adamw_hparams* hp, const zero_result* res_dev, hipStream_t stream)
+{
+    if (n < 0 || !hparams_ok(hp)) return ZERO_ERR_INVALID_ARGUMENT;
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !g || !param_out) return ZERO_ERR_INVALID_ARGUMENT;
+    const Layout L = make_layout(n, {reinterpret_cast<uintptr_t>(param_out)},
+                                 {reinterpret_cast<uintptr_t>(master), reinterpret_cast<uintptr_t>(exp_avg),
+                                  reinterpret_cast<uintptr_t>(exp_avg_sq), reinterpret_cast<uintptr_t>(g)});
+    const int grid = grid_for(layout_tiles(L), resident_grid_adamw());
+    return hip_status(launch_adamw(master, exp_avg, exp_avg_sq, g, static_cast<uint16_t*>(param_out), L,
+                                   derive(hp), res_dev, grid, stream));
+}
+
+size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp)) return 0;
+    if (T > 0 && tensors == nullptr) return 0;
+    for (int32_t t = 0; t < T; ++t)
+        if (tensors[t].n < 0) return 0;
+    return plan_offsets(tensors, T, M, two_pass_of(hp)).total;
+}
+
+int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
+              void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
+{
+    // ---- arguments
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr)
+        return ZERO_ERR_INVALID_ARGUMENT;
+    if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    int64_t total_n = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_tensor& x = tensors[t];
+        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        total_n += x.n;
+    }
+    const bool two_pass = two_pass_of(hp);
+    const int skip = hp->skip_on_nonfinite != 0;
+    if (total_n == 0)
+        return hip_status(
+            launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, nullptr, 0, stream));
+    if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    const PlanOffsets off = plan_offsets(tensors, T, M, two_pass);
+    if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+
+    // ---- the plan: header, tensor table, rank-pointer table (host image)
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    std::vector<uint8_t> blob(off.tiles, 0);
+    PlanHeader* hdr = reinterpret_cast<PlanHeader*>(blob.data());
+    TensorDesc* desc = reinterpret_cast<TensorDesc*>(blob.data() + off.desc);
+    const uint16_t** ptrs = reinterpret_cast<const uint16_t**>(blob.data() + off.ptrs);
+    int64_t tile = 0;
+    size_t gpos = off.gbuf;
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_tensor& x = tensors[t];
+        TensorDesc& d = desc[t];
+        d.grads = reinterpret_cast<const uint16_t* const*>(wsb + off.ptrs + sizeof(void*) * static_cast<size_t>(t) * M);
+        d.n = x.n;
+        d.tile_begin = tile;
+        if (x.n == 0) {
+            d.nvec = -1;
+            d.ntiles = 0;
+            continue;
+        }
+        std::vector<uintptr_t> b16, f32;
+        for (int32_t r = 0; r < M; ++r) {
+            ptrs[static_cast<size_t>(t) * M + r] = static_cast<const uint16_t*>(x.grads[r]);
+            b16.push_back(reinterpret_cast<uintptr_t>(x.grads[r]));
+        }
+        b16.push_back(reinterpret_cast<uintptr_t>(x.param_out));
+        f32 = {reinterpret_cast<uintptr_t>(x.master), reinterpret_cast<uintptr_t>(x.exp_avg),
+               reinterpret_cast<uintptr_t>(x.exp_avg_sq)};
+        const Layout L = make_layout(x.n, b16, f32);
+        d.master = x.master;
+        d.exp_avg = x.exp_avg;
+        d.exp_avg_sq = x.exp_avg_sq;
+        d.out = static_cast<uint16_t*>(x.param_out);
+        d.nvec = L.nvec;
+        d.head = L.head;
+        d.tail = L.tail;
+        d.ntiles = layout_tiles(L);
+        if (two_pass) {
+            // aligned with the other pointers at element `head`
+            const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
+            d.gbuf = reinterpret_cast<float*>(wsb + gpos + shift);
+            gpos += align_up((static_cast<size_t>(x.n) + 3) * 4, kAlign);
+        }
+        tile += d.ntiles;
+    }
+    const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
+    const int grid = grid_for(tile, resident_grid_fused(first_mode, M));
+    hdr->total_tiles = tile;
+    hdr->T = T;
+    hdr->M = M;
+    hdr->grid = grid;
+    hdr->two_pass = two_pass ? 1 : 0;
+    uint64_t sig = fnv1a(blob.data(), blob.size(), 1469598103934665603ull);
+    const uintptr_t wsaddr = reinterpret_cast<uintptr_t>(ws);
+    sig = fnv1a(reinterpret_cast<const uint8_t*>(&wsaddr), sizeof(wsaddr), sig);
+    if (sig == 0) sig = 1;
+    hdr->signature = sig;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
+    const auto key = std::make_pair(dev, wsaddr);
+    bool cached;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        auto it = g_plan_cache.find(key);
+        cached = it != g_plan_cache.end() && it->second == sig;
+    }
+    PlanHeader* hdr_dev = reinterpret_cast<PlanHeader*>(wsb);
+    TensorDesc* desc_dev = reinterpret_cast<TensorDesc*>(wsb + off.desc);
+    TileRef* tiles_dev = reinterpret_cast<TileRef*>(wsb + off.tiles);
+    Partial* parts_dev = reinterpret_cast<Partial*>(wsb + off.parts);
+    if (!cached) {
+        // tables first, tile map next, header (with the signature) last
+        WriteChunk c;
+        const size_t bytes_per = sizeof(c.data);
+        for (size_t pos = off.desc; pos < blob.size(); pos += bytes_per) {
+            const size_t len = (blob.size() - pos) < bytes_per ? (blob.size() - pos) : bytes_per;
+            c.offset = pos;
+            c.words = static_cast<uint32_t>(len / 4);
+            c.pad = 0;
+            std::memcpy(c.data, blob.data() + pos, len);
+            if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
+        }
+        if (launch_plan_tiles(desc_dev, T, tiles_dev, stream) != hipSuccess) return ZERO_ERR_HIP;
+        c.offset = 0;
+        c.words = static_cast<uint32_t>(off.desc / 4);
+        c.pad = 0;
+        std::memcpy(c.data, blob.data(), off.desc);
+        if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        g_plan_cache[key] = sig;
+    }
+
+    // ---- the step
+    const AdamScalars c = derive(hp);
+    const float gscale = static_cast<float>(hp->grad_scale);
+    hipError_t e = launch_fused(first_mode, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev,
+                                nullptr, grid, stream);
+    if (e != hipSuccess) return ZERO_ERR_HIP;
+    e = launch_finalize(parts_dev, grid, external_sumsq, hp->max_grad_norm, skip, res_dev, hdr_dev, sig, stream);
+    if (e != hipSuccess) return ZERO_ERR_HIP;
+    if (two_pass) {
+        const int grid_b = grid_for(tile, resident_grid_fused(Mode::PassB, M));
+        e = launch_fused(Mode::PassB, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev, res_dev,
+                         grid_b, stream);
+        if (e != hipSuccess) return ZERO_ERR_HIP;
+    }
+    return ZERO_OK;
+}
+
+int zero_workspace_forget(const void* ws)
+{
+    if (ws == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    forget_ws(ws);
+    return ZERO_OK;
+}
+
+}  // extern "C"

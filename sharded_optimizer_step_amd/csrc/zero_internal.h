@@ -1,0 +1,141 @@
+// zero_internal.h -- types shared by the host library and the gfx950 kernels
+// of the fused ZeRO-1 shard step. Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "zero_step.h"
+
+namespace zero {
+
+constexpr int kThreads = 256;                // one workgroup = 4 wave64
+constexpr int kVec = 8;                      // elements per vector: 16 B of bf16, 32 B of fp32
+constexpr int kTileElems = kThreads * kVec;  // 2048 elements per tile
+constexpr int kInlineRanks = 64;             // rank pointers passed by value per reduce pass
+constexpr int kMaxPartials = 8192;           // per-workgroup partial records of one launch
+constexpr size_t kAlign = 256;
+
+// fp32 scalars of one AdamW step, derived on the host in binary64 and
+// rounded once.
+struct AdamScalars {
+    float b1, omb1, b2, omb2;  // beta1, 1-beta1, beta2, 1-beta2
+    float decay;               // 1 - lr*weight_decay
+    float step_size;           // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;        // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+
+// How the elements of one shard are visited.
+//   vector mode (nvec >= 0): [0, head) one by one, then nvec 16-byte vectors of
+//     8 elements, then `tail` elements one by one; every pointer of the shard
+//     is 16-byte aligned at element `head`.
+//   scalar mode (nvec < 0): every element one by one (pointers that disagree
+//     on their alignment modulo 16 bytes).
+struct Layout {
+    int64_t n;
+    int64_t nvec;
+    int32_t head;
+    int32_t tail;
+};
+
+__host__ __device__ inline int64_t layout_tiles(const Layout& L)
+{
+    if (L.n <= 0) return 0;
+    if (L.nvec >= 0) {
+        const int64_t t = (L.nvec + kThreads - 1) / kThreads;
+        return t > 0 ? t : 1;
+    }
+    return (L.n + kTileElems - 1) / kTileElems;
+}
+
+// Upper bound of layout_tiles over every alignment of an n-element shard.
+__host__ __device__ inline int64_t tiles_bound(int64_t n) { return n <= 0 ? 0 : (n + kTileElems - 1) / kTileElems + 1; }
+
+// One tensor of a zero_step plan, as stored in the workspace.
+struct alignas(16) TensorDesc {
+    const uint16_t* const* grads;  // device address of this tensor's M rank pointers
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    uint16_t* out;
+    float* gbuf;                   // fp32 reduced gradient (two-pass plans), or null
+    int64_t n;
+    int64_t nvec;
+    int32_t head;
+    int32_t tail;
+    int64_t tile_begin;            // first global tile of this tensor
+    int64_t ntiles;
+};
+static_assert(sizeof(TensorDesc) == 96, "TensorDesc layout");
+
+struct TileRef {
+    int32_t tensor;
+    int32_t local;  // tile index within the tensor
+};
+
+struct alignas(16) Partial {
+    double sumsq;
+    uint32_t bad;
+    uint32_t pad;
+};
+
+struct alignas(16) PlanHeader {
+    uint64_t signature;
+    int64_t total_tiles;
+    int32_t T;
+    int32_t M;
+    int32_t grid;
+    int32_t two_pass;
+};
+
+// Byte offsets of the regions of a zero_step workspace.
+struct PlanOffsets {
+    size_t desc, ptrs, tiles, parts, gbuf, total;
+};
+
+// Payload of one plan-upload launch (carried in the kernel arguments).
+constexpr int kWriteWords = 500;
+struct WriteChunk {
+    uint64_t offset;  // byte offset in the workspace, 4-byte aligned
+    uint32_t words;
+    uint32_t pad;
+    uint32_t data[kWriteWords];
+};
+
+// Rank pointers passed by value to the flat reduce kernel.
+struct RankPtrs {
+    const uint16_t* p[kInlineRanks];
+};
+
+enum class Mode : int {
+    Full = 0,   // fold + unscale + check + AdamW + emit, one pass
+    PassA = 1,  // fold + unscale + check, store fp32 g
+    PassB = 2,  // read fp32 g, AdamW + emit (coefficient/skip from the result record)
+};
+
+// ---- launch wrappers (zero_kernels.hip); all return a hipError_t ----------
+
+hipError_t launch_reduce(const RankPtrs& ptrs, int Mc, bool first, bool last, float scale, const Layout& L,
+                         float* g_out, int grid, hipStream_t s);
+hipError_t launch_check(const float* g, const Layout& L, Partial* parts, int grid, hipStream_t s);
+hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint16_t* out, const Layout& L,
+                        const AdamScalars& c, const zero_result* res, int grid, hipStream_t s);
+hipError_t launch_finalize(const Partial* parts, int nparts, double external, double max_norm, int skip,
+                           zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s);
+hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s);
+hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipStream_t s);
+hipError_t launch_fused(Mode mode, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
+                        int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
+                        Partial* parts, const zero_result* res, int grid, hipStream_t s);
+
+// Workgroups of 256 threads that one kernel keeps resident on the current
+// device (occupancy x compute units), for the grid-stride launches.
+int resident_grid_reduce(int Mc, bool first);
+int resident_grid_check();
+int resident_grid_adamw();
+int resident_grid_fused(Mode mode, int M);
+
+}  // namespace zero

@@ -1,0 +1,658 @@
+// zero_kernels.hip -- gfx950 kernels of the fused ZeRO-1 shard step.
+//
+// The step ("CS336 Lecture 7: Parallelism 1", section "ZeRO Stage 1", steps
+// 2-4): the M bf16 gradient replicas of this rank's shard are summed in fp32
+// (the reduce-scatter arithmetic), unscaled, checked for inf/NaN and squared
+// into the global norm; AdamW then updates the fp32 master, m and v of the
+// shard (the 12 optimizer bytes of the table in section "训练内存的详细分析")
+// and the new master is rounded to the bf16 shard an all-gather would send.
+//
+// This is streaming, HBM-bound work with no contraction, so there is no MFMA
+// here. Design points for CDNA4:
+//  - 256-thread workgroups (4 wave64); each thread owns 8 consecutive
+//    elements, so every replica read is one 16-byte load and a wave reads a
+//    contiguous 1 KiB per replica.
+//  - Tiles of 2048 elements are dealt to workgroups grid-stride
+//    (tile = blockIdx.x + k*gridDim.x) with the grid sized to the resident
+//    capacity: all workgroups sweep the buffers together, which keeps the
+//    pages in flight few (TLB reach with 64+ streams) and the load balanced.
+//  - The rank fold is a fixed ascending left fold in fp32; the sum of squares
+//    uses exact binary64 squares, a per-thread binary64 accumulator, a fixed
+//    wave butterfly and a fixed LDS order, then a one-workgroup finalize over
+//    per-workgroup partials in index order: bitwise repeatable, no atomics.
+//  - Replica reads and the once-written outputs use non-temporal accesses.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "zero_internal.h"
+
+namespace zero {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ u32x4 ld_nt(const uint16_t* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st_nt(uint16_t* p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// bf16 -> fp32 is exact: the code is the upper half of the binary32 encoding.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf1(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+__device__ __forceinline__ void set8(float (&s)[8], u32x4 w)
+{
+    s[0] = bf_lo(w.x); s[1] = bf_hi(w.x); s[2] = bf_lo(w.y); s[3] = bf_hi(w.y);
+    s[4] = bf_lo(w.z); s[5] = bf_hi(w.z); s[6] = bf_lo(w.w); s[7] = bf_hi(w.w);
+}
+__device__ __forceinline__ void add8(float (&s)[8], u32x4 w)
+{
+    s[0] = s[0] + bf_lo(w.x); s[1] = s[1] + bf_hi(w.x); s[2] = s[2] + bf_lo(w.y); s[3] = s[3] + bf_hi(w.y);
+    s[4] = s[4] + bf_lo(w.z); s[5] = s[5] + bf_hi(w.z); s[6] = s[6] + bf_lo(w.w); s[7] = s[7] + bf_hi(w.w);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN with its sign.
+__device__ __forceinline__ uint32_t bf16_rne(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t nonfinite(float x) { return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u; }
+
+// Ascending left fold of the M replicas at elements [e0, e0+8). FROM0: start
+// from rank 0's value; otherwise continue the fold from s.
+template <int MT, bool FROM0>
+__device__ __forceinline__ void fold_vec(const uint16_t* const* __restrict__ gp, int M, int64_t e0, float (&s)[8])
+{
+    constexpr int B = 8;  // loads issued before the adds that consume them
+    const int Mr = MT > 0 ? MT : M;
+    if constexpr (FROM0) set8(s, ld_nt(gp[0] + e0));
+    auto batch = [&](int r0) {
+        u32x4 buf[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (r0 + j < Mr) buf[j] = ld_nt(gp[r0 + j] + e0);
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (r0 + j < Mr) add8(s, buf[j]);
+    };
+    if constexpr (MT > 0) {
+#pragma unroll
+        for (int r0 = FROM0 ? 1 : 0; r0 < MT; r0 += B) batch(r0);
+    } else {
+        for (int r0 = FROM0 ? 1 : 0; r0 < Mr; r0 += B) batch(r0);
+    }
+}
+
+template <int MT, bool FROM0>
+__device__ __forceinline__ float fold_one(const uint16_t* const* __restrict__ gp, int M, int64_t e, float s)
+{
+    const int Mr = MT > 0 ? MT : M;
+    if constexpr (FROM0) s = bf1(gp[0][e]);
+    for (int r = FROM0 ? 1 : 0; r < Mr; ++r) s = s + bf1(gp[r][e]);
+    return s;
+}
+
+// One AdamW element in fp32 (bias-corrected, eps outside the root, decay
+// decoupled and scaled by lr).
+__device__ __forceinline__ void adam1(float g, float coef, const AdamScalars& c, float& w, float& m, float& v)
+{
+    const float gc = g * coef;
+    m = fmaf(c.b1, m, c.omb1 * gc);
+    v = fmaf(c.b2, v, (c.omb2 * gc) * gc);
+    const float denom = fmaf(sqrtf(v), c.inv_sqrt_bc2, c.eps);
+    w = fmaf(w, c.decay, -(c.step_size * (m / denom)));
+}
+
+// Per-workgroup reduction of (sum of squares, non-finite flag) in a fixed
+// order, written to one partial record.
+__device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial* __restrict__ out)
+{
+    __shared__ double s_acc[kThreads / 64];
+    __shared__ uint32_t s_bad[kThreads / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        acc += __shfl_xor(acc, off, 64);
+        bad |= __shfl_xor(bad, off, 64);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_acc[wave] = acc;
+        s_bad[wave] = bad;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double a = s_acc[0];
+        uint32_t b = s_bad[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) {
+            a += s_acc[w];
+            b |= s_bad[w];
+        }
+        Partial p;
+        p.sumsq = a;
+        p.bad = b;
+        p.pad = 0;
+        *out = p;
+    }
+}
+
+// ------------------------------------------------------------------ tile body
+
+enum class Op : int { Reduce, Check, Adam, Full, PassA };
+
+// Pointers and layout of one shard, as seen by one tile.
+struct Ctx {
+    const uint16_t* const* gp;
+    int M;
+    float* master;
+    float* m;
+    float* v;
+    uint16_t* out;
+    float* gout;        // fp32 gradient written (Reduce, PassA)
+    const float* gin;   // fp32 gradient read (Check, Adam; Reduce continuing a fold)
+    int64_t n, nvec;
+    int32_t head, tail;
+};
+
+struct Scal {
+    float gscale;  // multiplier of the fp32 sum (applied when `last`)
+    float coef;    // clip coefficient (Adam, Full)
+    bool last;     // Reduce: this pass ends the fold
+};
+
+// One element, scalar path.
+template <Op OP, int MT, bool FROM0>
+__device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e, double& acc,
+                                       uint32_t& bad)
+{
+    float g;
+    if constexpr (OP == Op::Reduce) {
+        g = fold_one<MT, FROM0>(x.gp, x.M, e, FROM0 ? 0.0f : x.gin[e]);
+        if (k.last) g = g * k.gscale;
+        x.gout[e] = g;
+        return;
+    }
+    if constexpr (OP == Op::Full || OP == Op::PassA) g = fold_one<MT, true>(x.gp, x.M, e, 0.0f) * k.gscale;
+    if constexpr (OP == Op::Check || OP == Op::Adam) g = x.gin[e];
+    if constexpr (OP != Op::Adam) {
+        bad |= nonfinite(g);
+        const double d = static_cast<double>(g);
+        acc = fma(d, d, acc);
+    }
+    if constexpr (OP == Op::PassA) x.gout[e] = g;
+    if constexpr (OP == Op::Full || OP == Op::Adam) {
+        float w = x.master[e], m = x.m[e], v = x.v[e];
+        adam1(g, k.coef, c, w, m, v);
+        x.master[e] = w;
+        x.m[e] = m;
+        x.v[e] = v;
+        x.out[e] = static_cast<uint16_t>(bf16_rne(w));
+    }
+}
+
+// Eight elements [e0, e0+8), 16-byte vector path.
+template <Op OP, int MT, bool FROM0>
+__device__ __forceinline__ void do_vec(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0, double& acc,
+                                       uint32_t& bad)
+{
+    float g[8];
+    if constexpr (OP == Op::Reduce) {
+        if constexpr (!FROM0) {
+            const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
+            g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+        }
+        fold_vec<MT, FROM0>(x.gp, x.M, e0, g);
+        if (k.last) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g[j] = g[j] * k.gscale;
+        }
+        st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
+        st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
+        return;
+    }
+    if constexpr (OP == Op::Full || OP == Op::PassA) {
+        fold_vec<MT, true>(x.gp, x.M, e0, g);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[j] = g[j] * k.gscale;
+    }
+    if constexpr (OP == Op::Check || OP == Op::Adam) {
+        const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
+        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+    }
+    if constexpr (OP != Op::Adam) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bad |= nonfinite(g[j]);
+            const double d = static_cast<double>(g[j]);
+            acc = fma(d, d, acc);
+        }
+    }
+    if constexpr (OP == Op::PassA) {
+        st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
+        st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
+    }
+    if constexpr (OP == Op::Full || OP == Op::Adam) {
+        const f32x4 w0 = ld4(x.master + e0), w1 = ld4(x.master + e0 + 4);
+        const f32x4 m0 = ld4(x.m + e0), m1 = ld4(x.m + e0 + 4);
+        const f32x4 v0 = ld4(x.v + e0), v1 = ld4(x.v + e0 + 4);
+        float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) adam1(g[j], k.coef, c, w[j], m[j], v[j]);
+        st4(x.master + e0, f32x4{w[0], w[1], w[2], w[3]});
+        st4(x.master + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
+        st4(x.m + e0, f32x4{m[0], m[1], m[2], m[3]});
+        st4(x.m + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
+        st4(x.v + e0, f32x4{v[0], v[1], v[2], v[3]});
+        st4(x.v + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
+        u32x4 o;
+        o.x = bf16_rne(w[0]) | (bf16_rne(w[1]) << 16);
+        o.y = bf16_rne(w[2]) | (bf16_rne(w[3]) << 16);
+        o.z = bf16_rne(w[4]) | (bf16_rne(w[5]) << 16);
+        o.w = bf16_rne(w[6]) | (bf16_rne(w[7]) << 16);
+        st_nt(x.out + e0, o);
+    }
+}
+
+// Tile `t` of one shard.
+template <Op OP, int MT, bool FROM0>
+__device__ __forceinline__ void do_tile(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t t, double& acc,
+                                        uint32_t& bad)
+{
+    const int tid = threadIdx.x;
+    if (x.nvec >= 0) {
+        const int64_t v = t * kThreads + tid;
+        if (v < x.nvec) do_vec<OP, MT, FROM0>(x, k, c, x.head + v * kVec, acc, bad);
+        if (t == 0 && tid < x.head) do_one<OP, MT, FROM0>(x, k, c, tid, acc, bad);
+        const int64_t last = x.nvec > 0 ? (x.nvec - 1) / kThreads : 0;
+        if (t == last && tid < x.tail) do_one<OP, MT, FROM0>(x, k, c, x.head + x.nvec * kVec + tid, acc, bad);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+            const int64_t e = t * kTileElems + j * kThreads + tid;
+            if (e < x.n) do_one<OP, MT, FROM0>(x, k, c, e, acc, bad);
+        }
+    }
+}
+
+__device__ __forceinline__ Ctx ctx_of(const TensorDesc& d, int M)
+{
+    Ctx x;
+    x.gp = d.grads;
+    x.M = M;
+    x.master = d.master;
+    x.m = d.exp_avg;
+    x.v = d.exp_avg_sq;
+    x.out = d.out;
+    x.gout = d.gbuf;
+    x.gin = d.gbuf;
+    x.n = d.n;
+    x.nvec = d.nvec;
+    x.head = d.head;
+    x.tail = d.tail;
+    return x;
+}
+
+__device__ __forceinline__ Ctx ctx_flat(const Layout& L)
+{
+    Ctx x = {};
+    x.n = L.n;
+    x.nvec = L.nvec;
+    x.head = L.head;
+    x.tail = L.tail;
+    return x;
+}
+
+// ------------------------------------------------------------------ kernels
+
+template <int MT, bool FROM0>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(RankPtrs ptrs, int Mc, int last, float scale, Layout L,
+                                                          float* __restrict__ g_out)
+{
+    Ctx x = ctx_flat(L);
+    x.gp = ptrs.p;
+    x.M = Mc;
+    x.gout = g_out;
+    x.gin = g_out;
+    const Scal k{scale, 1.0f, last != 0};
+    const AdamScalars c{};
+    double acc = 0.0;
+    uint32_t bad = 0;
+    const int64_t tiles = layout_tiles(L);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Reduce, MT, FROM0>(x, k, c, t, acc, bad);
+}
+
+__global__ __launch_bounds__(kThreads) void check_kernel(const float* __restrict__ g, Layout L,
+                                                         Partial* __restrict__ parts)
+{
+    Ctx x = ctx_flat(L);
+    x.gin = g;
+    const Scal k{1.0f, 1.0f, false};
+    const AdamScalars c{};
+    double acc = 0.0;
+    uint32_t bad = 0;
+    const int64_t tiles = layout_tiles(L);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Check, 1, true>(x, k, c, t, acc, bad);
+    block_partial(acc, bad, parts + blockIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ master, float* __restrict__ m,
+                                                         float* __restrict__ v, const float* __restrict__ g,
+                                                         uint16_t* __restrict__ out, Layout L, AdamScalars c,
+                                                         const zero_result* __restrict__ res)
+{
+    float coef = 1.0f;
+    if (res != nullptr) {
+        if (res->skipped != 0 || res->status != 0) return;
+        coef = res->clip_coef;
+    }
+    Ctx x = ctx_flat(L);
+    x.master = master;
+    x.m = m;
+    x.v = v;
+    x.out = out;
+    x.gin = g;
+    const Scal k{1.0f, coef, false};
+    double acc = 0.0;
+    uint32_t bad = 0;
+    const int64_t tiles = layout_tiles(L);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Adam, 1, true>(x, k, c, t, acc, bad);
+}
+
+template <Mode MODE, int MT>
+__global__ __launch_bounds__(kThreads) void fused_kernel(const PlanHeader* __restrict__ hdr,
+                                                         const TensorDesc* __restrict__ desc,
+                                                         const TileRef* __restrict__ tiles, int64_t total_tiles,
+                                                         uint64_t sig, int M, float gscale, AdamScalars c,
+                                                         Partial* __restrict__ parts,
+                                                         const zero_result* __restrict__ res)
+{
+    if (hdr->signature != sig) return;  // the workspace no longer holds this plan: write nothing
+    float coef = 1.0f;
+    if constexpr (MODE == Mode::PassB) {
+        if (res->skipped != 0 || res->status != 0) return;
+        coef = res->clip_coef;
+    }
+    constexpr Op OP = MODE == Mode::Full ? Op::Full : (MODE == Mode::PassA ? Op::PassA : Op::Adam);
+    const Scal k{gscale, coef, false};
+    double acc = 0.0;
+    uint32_t bad = 0;
+    for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+        const TileRef tr = tiles[t];
+        const Ctx x = ctx_of(desc[tr.tensor], M);
+        do_tile<OP, MT, true>(x, k, c, tr.local, acc, bad);
+    }
+    if constexpr (MODE != Mode::PassB) block_partial(acc, bad, parts + blockIdx.x);
+}
+
+// One workgroup: combine the partials in index order, then the norm, the
+// clip coefficient and the skip decision.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __restrict__ parts, int nparts,
+                                                            double external, double max_norm, int skip,
+                                                            zero_result* __restrict__ res,
+                                                            const PlanHeader* __restrict__ hdr, uint64_t sig)
+{
+    if (hdr != nullptr && hdr->signature != sig) {
+        if (threadIdx.x == 0) {
+            zero_result r;
+            r.sumsq = __builtin_nan("");
+            r.grad_norm = __builtin_nanf("");
+            r.clip_coef = __builtin_nanf("");
+            r.found_inf = 0;
+            r.skipped = 1;
+            r.status = ZERO_ERR_STALE_WORKSPACE;
+            r.reserved = 0;
+            *res = r;
+        }
+        return;
+    }
+    double acc = 0.0;
+    uint32_t bad = 0;
+    for (int i = threadIdx.x; i < nparts; i += kThreads) {
+        acc += parts[i].sumsq;
+        bad |= parts[i].bad;
+    }
+    __shared__ Partial s_total;
+    block_partial(acc, bad, &s_total);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double total = s_total.sumsq + external;
+        const double norm = sqrt(total);
+        double coef = 1.0;
+        if (max_norm > 0.0) {
+            coef = max_norm / (norm + 1e-6);
+            if (coef > 1.0) coef = 1.0;  // a NaN coefficient stays NaN
+        }
+        zero_result r;
+        r.sumsq = total;
+        r.grad_norm = static_cast<float>(norm);
+        r.clip_coef = static_cast<float>(coef);
+        r.found_inf = s_total.bad != 0 ? 1 : 0;
+        r.skipped = (s_total.bad != 0 && skip != 0) ? 1 : 0;
+        r.status = ZERO_OK;
+        r.reserved = 0;
+        *res = r;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void plan_write_kernel(uint8_t* __restrict__ ws, WriteChunk c)
+{
+    uint32_t* dst = reinterpret_cast<uint32_t*>(ws + c.offset);
+    for (uint32_t i = threadIdx.x; i < c.words; i += kThreads) dst[i] = c.data[i];
+}
+
+__global__ __launch_bounds__(kThreads) void plan_tiles_kernel(const TensorDesc* __restrict__ desc, int T,
+                                                              TileRef* __restrict__ tiles)
+{
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+        const int64_t b = desc[t].tile_begin, nt = desc[t].ntiles;
+        for (int64_t j = threadIdx.x; j < nt; j += kThreads) {
+            TileRef r;
+            r.tensor = t;
+            r.local = static_cast<int32_t>(j);
+            tiles[b + j] = r;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ occupancy
+
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+// Resident workgroups of one kernel on the current device, cached per
+// (kernel, device).
+template <typename K>
+int resident(K kernel)
+{
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_pair(reinterpret_cast<const void*>(kernel), dev);
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    int g = per_cu * device_cus();
+    g = g < kMaxPartials ? g : kMaxPartials;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = g;
+    return g;
+}
+
+template <bool FROM0>
+hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, const Layout& L, float* g_out,
+                           int grid, hipStream_t s)
+{
+    switch (Mc) {
+    case 1: reduce_kernel<1, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 2: reduce_kernel<2, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 4: reduce_kernel<4, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 8: reduce_kernel<8, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 16: reduce_kernel<16, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 32: reduce_kernel<32, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    case 64: reduce_kernel<64, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    default: reduce_kernel<0, FROM0><<<grid, kThreads, 0, s>>>(ptrs, Mc, last, scale, L, g_out); break;
+    }
+    return hipGetLastError();
+}
+
+template <Mode MODE>
+hipError_t fused_dispatch(const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles, int64_t total_tiles,
+                          uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
+                          const zero_result* res, int grid, hipStream_t s)
+{
+#define ZERO_FUSED(MTV)                                                                                       \
+    fused_kernel<MODE, MTV><<<grid, kThreads, 0, s>>>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, \
+                                                      res)
+    if constexpr (MODE == Mode::PassB) {
+        ZERO_FUSED(1);
+    } else {
+        switch (M) {
+        case 1: ZERO_FUSED(1); break;
+        case 2: ZERO_FUSED(2); break;
+        case 4: ZERO_FUSED(4); break;
+        case 8: ZERO_FUSED(8); break;
+        case 16: ZERO_FUSED(16); break;
+        case 32: ZERO_FUSED(32); break;
+        case 64: ZERO_FUSED(64); break;
+        default: ZERO_FUSED(0); break;
+        }
+    }
+#undef ZERO_FUSED
+    return hipGetLastError();
+}
+
+template <Mode MODE>
+int fused_resident(int M)
+{
+    if constexpr (MODE == Mode::PassB) {
+        return resident(fused_kernel<MODE, 1>);
+    } else {
+        switch (M) {
+        case 1: return resident(fused_kernel<MODE, 1>);
+        case 2: return resident(fused_kernel<MODE, 2>);
+        case 4: return resident(fused_kernel<MODE, 4>);
+        case 8: return resident(fused_kernel<MODE, 8>);
+        case 16: return resident(fused_kernel<MODE, 16>);
+        case 32: return resident(fused_kernel<MODE, 32>);
+        case 64: return resident(fused_kernel<MODE, 64>);
+        default: return resident(fused_kernel<MODE, 0>);
+        }
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ wrappers
+
+hipError_t launch_reduce(const RankPtrs& ptrs, int Mc, bool first, bool last, float scale, const Layout& L,
+                         float* g_out, int grid, hipStream_t s)
+{
+    if (first) return reduce_dispatch<true>(ptrs, Mc, last ? 1 : 0, scale, L, g_out, grid, s);
+    return reduce_dispatch<false>(ptrs, Mc, last ? 1 : 0, scale, L, g_out, grid, s);
+}
+
+hipError_t launch_check(const float* g, const Layout& L, Partial* parts, int grid, hipStream_t s)
+{
+    check_kernel<<<grid, kThreads, 0, s>>>(g, L, parts);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint16_t* out, const Layout& L,
+                        const AdamScalars& c, const zero_result* res, int grid, hipStream_t s)
+{
+    adamw_kernel<<<grid, kThreads, 0, s>>>(master, m, v, g, out, L, c, res);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const Partial* parts, int nparts, double external, double max_norm, int skip,
+                           zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s)
+{
+    finalize_kernel<<<1, kThreads, 0, s>>>(parts, nparts, external, max_norm, skip, res, hdr, sig);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s)
+{
+    plan_write_kernel<<<1, kThreads, 0, s>>>(ws, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipStream_t s)
+{
+    const int grid = T < 4096 ? (T > 0 ? T : 1) : 4096;
+    plan_tiles_kernel<<<grid, kThreads, 0, s>>>(desc, T, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(Mode mode, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
+                        int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
+                        Partial* parts, const zero_result* res, int grid, hipStream_t s)
+{
+    switch (mode) {
+    case Mode::Full:
+        return fused_dispatch<Mode::Full>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+    case Mode::PassA:
+        return fused_dispatch<Mode::PassA>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+    case Mode::PassB:
+        return fused_dispatch<Mode::PassB>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+int resident_grid_reduce(int Mc, bool first)
+{
+    // every instantiation has the same launch bounds; the widest one decides
+    (void)Mc;
+    return first ? resident(reduce_kernel<64, true>) : resident(reduce_kernel<64, false>);
+}
+
+int resident_grid_check() { return resident(check_kernel); }
+int resident_grid_adamw() { return resident(adamw_kernel); }
+
+int resident_grid_fused(Mode mode, int M)
+{
+    switch (mode) {
+    case Mode::Full: return fused_resident<Mode::Full>(M);
+    case Mode::PassA: return fused_resident<Mode::PassA>(M);
+    case Mode::PassB: return fused_resident<Mode::PassB>(M);
+    }
+    return 1;
+}
+
+}  // namespace zero

@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/*.h declares, and rejects bad arguments before touching the GPU.
+No call here launches a kernel."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import sharded_optimizer_step_amd as z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(zero_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def exported_symbols(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(names) == set(z.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    syms = exported_symbols(z.LIB_PATH)
+    missing = [n for n in declared_functions() if n not in syms]
+    assert not missing, missing
+    L = z.lib()
+    for n in declared_functions():
+        assert getattr(L, n) is not None
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Compile the header with gcc and compare every field offset with the
+    ctypes mirrors of the Python binding."""
+    import subprocess
+    fields = {"zero_adamw_hparams": z._CHparams, "zero_tensor": z._CTensor}
+    body = []
+    for cname, cls in fields.items():
+        body.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            body.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    body.append('printf("zero_result %zu\\n", sizeof(zero_result));')
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"zero_step.h\"\nint main(void){" +
+                   "".join(body) + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    "-o", str(exe), str(src)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for cname, cls in fields.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+    assert int(got["zero_result"]) == z.RESULT_BYTES
+
+
+def test_status_strings():
+    assert z.zero_status_string(0) == "ok"
+    assert "workspace" in z.zero_status_string(2)
+    assert "stale" in z.zero_status_string(4) or "no longer" in z.zero_status_string(4)
+    assert z.zero_status_string(99) == "unknown status"
+
+
+def _hp(**kw):
+    return z.HParams(**kw)._c()
+
+
+@pytest.mark.parametrize("kw", [dict(lr=-1.0), dict(lr=float("nan")), dict(beta1=1.0), dict(beta2=-0.1),
+                                dict(eps=-1e-8), dict(step=0), dict(grad_scale=0.0),
+                                dict(grad_scale=float("inf")), dict(max_grad_norm=float("nan")),
+                                dict(weight_decay=float("inf"))])
+def test_bad_hparams_are_rejected_without_launch(kw):
+    L = z.lib()
+    h = _hp(**kw)
+    assert L.zero_adamw_step(None, None, None, None, None, 10, ctypes.byref(h), None, None) == 1
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(10, None, None, None, None, None)
+    assert L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h)) == 0
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, None, 0, ctypes.c_void_p(256), None) == 1
+
+
+def test_reserved_field_must_be_zero():
+    L = z.lib()
+    h = _hp()
+    h.reserved = 1
+    assert L.zero_adamw_step(None, None, None, None, None, 10, ctypes.byref(h), None, None) == 1
+
+
+def test_shard_reduce_argument_checks():
+    L = z.lib()
+    fake = (ctypes.c_void_p * 2)(256, 512)
+    assert L.zero_shard_reduce(fake, 0, 10, 1.0, 1024, None) == 1          # M < 1
+    assert L.zero_shard_reduce(fake, 65537, 10, 1.0, 1024, None) == 1      # M too large
+    assert L.zero_shard_reduce(fake, 2, -1, 1.0, 1024, None) == 1          # n < 0
+    assert L.zero_shard_reduce(fake, 2, 10, 0.0, 1024, None) == 1          # scale <= 0
+    assert L.zero_shard_reduce(fake, 2, 10, float("nan"), 1024, None) == 1
+    assert L.zero_shard_reduce(None, 2, 10, 1.0, 1024, None) == 1          # no replica array
+    assert L.zero_shard_reduce(fake, 2, 10, 1.0, None, None) == 1          # no output
+    nul = (ctypes.c_void_p * 2)(256, None)
+    assert L.zero_shard_reduce(nul, 2, 10, 1.0, 1024, None) == 1          # a null replica
+    assert L.zero_shard_reduce(fake, 2, 0, 1.0, None, None) == 0           # n == 0: no-op
+
+
+def test_adamw_and_check_argument_checks():
+    L = z.lib()
+    h = _hp()
+    assert L.zero_adamw_step(None, None, None, None, None, 0, ctypes.byref(h), None, None) == 0  # n == 0
+    assert L.zero_adamw_step(256, 256, 256, None, 256, 5, ctypes.byref(h), None, None) == 1      # no g
+    assert L.zero_adamw_step(256, 256, 256, 256, 256, -1, ctypes.byref(h), None, None) == 1
+    assert L.zero_grad_check_norm(256, 10, None, 0.0, None, 1 << 20, None, None) == 1            # no result
+    assert L.zero_grad_check_norm(256, 10, None, 0.0, None, 1 << 20, 512, None) == 1             # no ws
+    assert L.zero_grad_check_norm(256, 10, None, 0.0, 1024, 16, 512, None) == 2                  # ws short
+    assert L.zero_grad_check_norm_workspace_bytes(0) == 0
+    assert L.zero_grad_check_norm_workspace_bytes(1) > 0
+
+
+def test_zero_step_argument_checks():
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(100, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    assert need > 100 * 4  # two-pass: holds the fp32 reduced gradient
+    res = ctypes.c_void_p(1 << 20)
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, 1 << 24, need - 1, res, None) == 2   # ws short
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, (1 << 24) + 16, need, res, None) == 1  # ws misaligned
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, None, need, res, None) == 1          # no ws
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, 1 << 24, need, None, None) == 1       # no result
+    assert L.zero_step(arr, -1, 2, ctypes.byref(h), 0.0, 1 << 24, need, res, None) == 1
+    assert L.zero_step(arr, 1, 0, ctypes.byref(h), 0.0, 1 << 24, need, res, None) == 1
+    nul = (ctypes.c_void_p * 2)(256, None)
+    arr2 = (z._CTensor * 1)()
+    arr2[0] = z._CTensor(100, ctypes.cast(nul, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    assert L.zero_step(arr2, 1, 2, ctypes.byref(h), 0.0, 1 << 24, need, res, None) == 1      # null replica
+    arr3 = (z._CTensor * 1)()
+    arr3[0] = z._CTensor(-5, None, None, None, None, None)
+    assert L.zero_step_workspace_bytes(arr3, 1, 2, ctypes.byref(h)) == 0
+
+
+def test_workspace_sizes_follow_the_traffic_plan():
+    one = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams())
+    two = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams(max_grad_norm=1.0))
+    skip = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams(skip_on_nonfinite=1))
+    # the single pass keeps no gradient; clip or skip keeps the fp32 reduced gradient once
+    assert one < 1_000_000
+    assert two - one >= 4 * 1_000_000 and skip == two
+    ragged = z.zero_step_workspace_bytes_for_sizes([512, 0, 4099, 11011], 8, z.HParams(max_grad_norm=1.0))
+    assert ragged >= 4 * (512 + 4099 + 11011)
+
+
+def test_forget_needs_a_pointer():
+    L = z.lib()
+    assert L.zero_workspace_forget(None) == 1
+    assert L.zero_workspace_forget(ctypes.c_void_p(4096)) == 0
