@@ -1,0 +1,205 @@
+"""Benchmark of the fused per-rank ZeRO-1 shard step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
+
+A step is one zero_step call over the workload's shard: fold the M bf16
+gradient replicas in fp32, unscale, check, norm (+ clip/skip when the
+workload asks), AdamW on the fp32 master/m/v, bf16 emit. Inputs are seeded
+synthetic data generated on the device before the timed region. The default
+workload is the 7.5B-parameter model at 64-way ZeRO-1: one rank's
+117,187,500-parameter shard reducing 64 replicas.
+
+Prints one JSON line: params updated per second, the live HBM roofline of
+the step kernels (algorithmic bytes / average step duration from HIP events
+on the launch stream), the counter-measured HBM traffic when a profile of the
+current kernel source is on file, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+METRIC = "params updated/s + HBM GB/s (% of peak), fused ZeRO-1 reduce+AdamW shard step"
+KERNEL_SRC = os.path.join(ROOT, "sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=2, help="0..4, see synth/workloads.py")
+    p.add_argument("--cpu-sample", type=int, default=1 << 26,
+                   help="elements of the shard the CPU oracle runs on (0: skip the CPU baseline)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain 4 GiB device copy (HBM counter calibration)")
+    p.add_argument("--stagger", type=int, default=0, help="bytes added between consecutive replica bases")
+    return p.parse_args()
+
+
+def calib_copy(steps: int):
+    import torch
+    n = 1 << 30  # 4 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "launches": steps}))
+
+
+def build_workload(w, stagger: int):
+    import torch
+
+    import sharded_optimizer_step_amd as z
+    import synth
+
+    dev = torch.device("cuda:0")
+    tensors = []
+    for spec in w.tensors:
+        n = spec.n
+        grads = []
+        if stagger:
+            # one allocation, rows padded to 256 B plus a per-row stagger
+            row = (2 * n + 255) // 256 * 256 + stagger
+            assert row % 16 == 0
+            packed = torch.empty(w.M * row // 2, dtype=torch.bfloat16, device=dev)
+            rows = [packed[r * row // 2:r * row // 2 + n] for r in range(w.M)]
+        else:
+            rows = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(w.M)]
+        for r, g in enumerate(rows):
+            st = synth.stream_id(synth.KIND_GRAD, spec.tensor_id, r)
+            synth.device_bf16(g, w.seed, st, w.grad_std, start=spec.start)
+            grads.append(g)
+        st = lambda k: synth.stream_id(k, spec.tensor_id, 0)
+        master = synth.device_f32(torch.empty(n, device=dev), w.seed, st(synth.KIND_MASTER), w.master_std,
+                                  start=spec.start)
+        m = torch.zeros(n, device=dev)
+        v = torch.zeros(n, device=dev)
+        if w.m_std:
+            synth.device_f32(m, w.seed, st(synth.KIND_EXP_AVG), w.m_std, start=spec.start)
+        if w.v_std:
+            synth.device_f32(v, w.seed, st(synth.KIND_EXP_AVG_SQ), w.v_std, start=spec.start, absval=True)
+        out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        tensors.append(z.ZeroTensor(grads, master, m, v, out))
+    torch.cuda.synchronize()
+    return tensors
+
+
+def cpu_baseline(w, sample: int) -> dict:
+    """The oracle, as it is, on the first `sample` elements of the workload's
+    first tensor, with all M replicas, on one host core."""
+    import oracle
+    import synth
+
+    spec = w.tensors[0]
+    S = min(sample, spec.n)
+    st = lambda k, r=0: synth.stream_id(k, spec.tensor_id, r)
+    grads = [synth.host_bf16(S, w.seed, st(synth.KIND_GRAD, r), w.grad_std, start=spec.start) for r in range(w.M)]
+    import numpy as np
+    master = synth.host_f32(S, w.seed, st(synth.KIND_MASTER), w.master_std, start=spec.start)
+    m = synth.host_f32(S, w.seed, st(synth.KIND_EXP_AVG), w.m_std, start=spec.start) if w.m_std else \
+        np.zeros(S, np.float32)
+    v = synth.host_f32(S, w.seed, st(synth.KIND_EXP_AVG_SQ), w.v_std, start=spec.start, absval=True) if w.v_std \
+        else np.zeros(S, np.float32)
+    hp = oracle.HParams(**{k: val for k, val in w.hparams().items()})
+    t0 = time.perf_counter()
+    oracle.zero_step([oracle.TensorState(grads, master, m, v, None)], hp)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {S:,} elements of the shard with all {w.M} replicas ({dt:.1f} s, single thread)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+              "the multi-GPU layout is a design, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sharded_optimizer_step_amd as z
+    from synth.workloads import workload
+
+    torch.cuda.set_device(0)
+    if a.calib_copy:
+        calib_copy(max(a.steps, 1))
+        return
+    w = workload(a.workload)
+    tensors = build_workload(w, a.stagger)
+    hp0 = w.hparams()
+    hp = z.HParams(**hp0)
+    ws = z.workspace(z.zero_step_workspace_bytes(tensors, w.M, hp))
+    res = z.new_result()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        hp.step = hp0["step"] + i
+        z.zero_step(tensors, hp, 0.0, ws, res, stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    r = z.read_result(res)
+    if r["status"] != 0:
+        raise RuntimeError(f"step status {r}")
+    K = a.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(a.warmup + i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per_ms = sorted(s.elapsed_time(e) for s, e in ev)
+    avg_ms = sum(per_ms) / K
+    n = w.n_total
+    bpp = w.bytes_per_param()
+    achieved = bpp * n / (avg_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        ent = tf.get(str(a.workload))
+        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = ent["bytes_per_launch"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    cpu = None
+    if a.cpu_sample > 0:
+        cpu = cpu_baseline(w, a.cpu_sample)
+    line = {
+        "metric": METRIC, "value": n / (total_ms * 1e-3 / K), "unit": "params/s", "n_gpus": 1, "steps": K,
+        "warmup": a.warmup, "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "shard_params": n, "M": w.M, "tensors": len(w.tensors),
+                   "bytes_per_param": bpp, "two_pass": w.two_pass, "step_t": hp0["step"],
+                   "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
+                   "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

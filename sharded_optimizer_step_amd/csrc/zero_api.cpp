@@ -90,6 +90,20 @@ int grid_for(int64_t tiles, int resident)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
 
+// The fused kernels' geometry: the longest per-replica bursts (largest tile)
+// that still give every compute unit at least one tile; small buckets fall
+// back to 2048-element tiles.
+int pick_geom(const std::vector<Layout>& layouts, int cus)
+{
+    for (int g = kNumGeoms - 1; g > 0; --g) {
+        const int64_t tv = static_cast<int64_t>(kGeoms[g].nt) * kGeoms[g].u;
+        int64_t tiles = 0;
+        for (const Layout& L : layouts) tiles += layout_tiles(L, tv);
+        if (tiles >= cus) return g;
+    }
+    return 0;
+}
+
 // ------------------------------------------------------------------ plans
 
 PlanOffsets plan_offsets(const zero_tensor* ts, int32_t T, int32_t M, bool two_pass)
@@ -256,6 +270,24 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     PlanHeader* hdr = reinterpret_cast<PlanHeader*>(blob.data());
     TensorDesc* desc = reinterpret_cast<TensorDesc*>(blob.data() + off.desc);
     const uint16_t** ptrs = reinterpret_cast<const uint16_t**>(blob.data() + off.ptrs);
+    std::vector<Layout> layouts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_tensor& x = tensors[t];
+        if (x.n == 0) {
+            layouts[t] = Layout{0, -1, 0, 0};
+            continue;
+        }
+        std::vector<uintptr_t> b16, f32;
+        for (int32_t r = 0; r < M; ++r) b16.push_back(reinterpret_cast<uintptr_t>(x.grads[r]));
+        b16.push_back(reinterpret_cast<uintptr_t>(x.param_out));
+        f32 = {reinterpret_cast<uintptr_t>(x.master), reinterpret_cast<uintptr_t>(x.exp_avg),
+               reinterpret_cast<uintptr_t>(x.exp_avg_sq)};
+        layouts[t] = make_layout(x.n, b16, f32);
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
+    const int geom = pick_geom(layouts, compute_units());
+    const int64_t tile_vecs = static_cast<int64_t>(kGeoms[geom].nt) * kGeoms[geom].u;
     int64_t tile = 0;
     size_t gpos = off.gbuf;
     for (int32_t t = 0; t < T; ++t) {
@@ -269,15 +301,9 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
             d.ntiles = 0;
             continue;
         }
-        std::vector<uintptr_t> b16, f32;
-        for (int32_t r = 0; r < M; ++r) {
+        for (int32_t r = 0; r < M; ++r)
             ptrs[static_cast<size_t>(t) * M + r] = static_cast<const uint16_t*>(x.grads[r]);
-            b16.push_back(reinterpret_cast<uintptr_t>(x.grads[r]));
-        }
-        b16.push_back(reinterpret_cast<uintptr_t>(x.param_out));
-        f32 = {reinterpret_cast<uintptr_t>(x.master), reinterpret_cast<uintptr_t>(x.exp_avg),
-               reinterpret_cast<uintptr_t>(x.exp_avg_sq)};
-        const Layout L = make_layout(x.n, b16, f32);
+        const Layout& L = layouts[t];
         d.master = x.master;
         d.exp_avg = x.exp_avg;
         d.exp_avg_sq = x.exp_avg_sq;
@@ -285,7 +311,7 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
         d.nvec = L.nvec;
         d.head = L.head;
         d.tail = L.tail;
-        d.ntiles = layout_tiles(L);
+        d.ntiles = layout_tiles(L, tile_vecs);
         if (two_pass) {
             // aligned with the other pointers at element `head`
             const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
@@ -295,20 +321,19 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
         tile += d.ntiles;
     }
     const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
-    const int grid = grid_for(tile, resident_grid_fused(first_mode, M));
+    const int grid = grid_for(tile, resident_grid_fused(first_mode, geom));
     hdr->total_tiles = tile;
     hdr->T = T;
     hdr->M = M;
     hdr->grid = grid;
     hdr->two_pass = two_pass ? 1 : 0;
+    hdr->geom = geom;
     uint64_t sig = fnv1a(blob.data(), blob.size(), 1469598103934665603ull);
     const uintptr_t wsaddr = reinterpret_cast<uintptr_t>(ws);
     sig = fnv1a(reinterpret_cast<const uint8_t*>(&wsaddr), sizeof(wsaddr), sig);
     if (sig == 0) sig = 1;
     hdr->signature = sig;
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
     const auto key = std::make_pair(dev, wsaddr);
     bool cached;
     {
@@ -345,14 +370,14 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     // ---- the step
     const AdamScalars c = derive(hp);
     const float gscale = static_cast<float>(hp->grad_scale);
-    hipError_t e = launch_fused(first_mode, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev,
+    hipError_t e = launch_fused(first_mode, geom, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev,
                                 nullptr, grid, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
     e = launch_finalize(parts_dev, grid, external_sumsq, hp->max_grad_norm, skip, res_dev, hdr_dev, sig, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
     if (two_pass) {
-        const int grid_b = grid_for(tile, resident_grid_fused(Mode::PassB, M));
-        e = launch_fused(Mode::PassB, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev, res_dev,
+        const int grid_b = grid_for(tile, resident_grid_fused(Mode::PassB, geom));
+        e = launch_fused(Mode::PassB, geom, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev, res_dev,
                          grid_b, stream);
         if (e != hipSuccess) return ZERO_ERR_HIP;
     }

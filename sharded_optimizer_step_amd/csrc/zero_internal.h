@@ -41,15 +41,29 @@ struct Layout {
     int32_t tail;
 };
 
-__host__ __device__ inline int64_t layout_tiles(const Layout& L)
+// Tiles of `tile_vecs` vectors (8 elements each) covering one shard.
+__host__ __device__ inline int64_t layout_tiles(const Layout& L, int64_t tile_vecs = kThreads)
 {
     if (L.n <= 0) return 0;
     if (L.nvec >= 0) {
-        const int64_t t = (L.nvec + kThreads - 1) / kThreads;
+        const int64_t t = (L.nvec + tile_vecs - 1) / tile_vecs;
         return t > 0 ? t : 1;
     }
-    return (L.n + kTileElems - 1) / kTileElems;
+    const int64_t te = tile_vecs * kVec;
+    return (L.n + te - 1) / te;
 }
+
+// Geometry of the fused kernels: NT threads per workgroup, U vectors per
+// thread per tile. Within a tile, thread (wave w, lane l) owns vectors
+// w*64*U + u*64 + l (u < U): each load instruction of a wave reads 1 KiB
+// contiguous, and the workgroup reads NT*U*16 contiguous bytes of one replica
+// before any wave moves on to the next replica.
+struct Geom {
+    int nt;
+    int u;
+};
+constexpr Geom kGeoms[] = {{256, 1}, {1024, 1}, {1024, 2}, {1024, 4}, {1024, 8}};
+constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 
 // Upper bound of layout_tiles over every alignment of an n-element shard.
 __host__ __device__ inline int64_t tiles_bound(int64_t n) { return n <= 0 ? 0 : (n + kTileElems - 1) / kTileElems + 1; }
@@ -89,6 +103,8 @@ struct alignas(16) PlanHeader {
     int32_t M;
     int32_t grid;
     int32_t two_pass;
+    int32_t geom;  // index into kGeoms
+    int32_t pad;
 };
 
 // Byte offsets of the regions of a zero_step workspace.
@@ -127,7 +143,7 @@ hipError_t launch_finalize(const Partial* parts, int nparts, double external, do
                            zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s);
 hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s);
 hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipStream_t s);
-hipError_t launch_fused(Mode mode, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
+hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
                         int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
                         Partial* parts, const zero_result* res, int grid, hipStream_t s);
 
@@ -136,6 +152,7 @@ hipError_t launch_fused(Mode mode, const PlanHeader* hdr, const TensorDesc* desc
 int resident_grid_reduce(int Mc, bool first);
 int resident_grid_check();
 int resident_grid_adamw();
-int resident_grid_fused(Mode mode, int M);
+int resident_grid_fused(Mode mode, int geom);
+int compute_units();  // of the current device
 
 }  // namespace zero

@@ -123,10 +123,11 @@ __device__ __forceinline__ void adam1(float g, float coef, const AdamScalars& c,
 
 // Per-workgroup reduction of (sum of squares, non-finite flag) in a fixed
 // order, written to one partial record.
+template <int NT = kThreads>
 __device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial* __restrict__ out)
 {
-    __shared__ double s_acc[kThreads / 64];
-    __shared__ uint32_t s_bad[kThreads / 64];
+    __shared__ double s_acc[NT / 64];
+    __shared__ uint32_t s_bad[NT / 64];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         acc += __shfl_xor(acc, off, 64);
@@ -142,7 +143,7 @@ __device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial*
         double a = s_acc[0];
         uint32_t b = s_bad[0];
 #pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w) {
+        for (int w = 1; w < NT / 64; ++w) {
             a += s_acc[w];
             b |= s_bad[w];
         }
@@ -208,6 +209,32 @@ __device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamSc
     }
 }
 
+// AdamW + bf16 emit of elements [e0, e0+8) from their gradient g.
+__device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0,
+                                      const float (&g)[8])
+{
+    const f32x4 w0 = ld4(x.master + e0), w1 = ld4(x.master + e0 + 4);
+    const f32x4 m0 = ld4(x.m + e0), m1 = ld4(x.m + e0 + 4);
+    const f32x4 v0 = ld4(x.v + e0), v1 = ld4(x.v + e0 + 4);
+    float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) adam1(g[j], k.coef, c, w[j], m[j], v[j]);
+    st4(x.master + e0, f32x4{w[0], w[1], w[2], w[3]});
+    st4(x.master + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
+    st4(x.m + e0, f32x4{m[0], m[1], m[2], m[3]});
+    st4(x.m + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
+    st4(x.v + e0, f32x4{v[0], v[1], v[2], v[3]});
+    st4(x.v + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
+    u32x4 o;
+    o.x = bf16_rne(w[0]) | (bf16_rne(w[1]) << 16);
+    o.y = bf16_rne(w[2]) | (bf16_rne(w[3]) << 16);
+    o.z = bf16_rne(w[4]) | (bf16_rne(w[5]) << 16);
+    o.w = bf16_rne(w[6]) | (bf16_rne(w[7]) << 16);
+    st_nt(x.out + e0, o);
+}
+
 // Eight elements [e0, e0+8), 16-byte vector path.
 template <Op OP, int MT, bool FROM0>
 __device__ __forceinline__ void do_vec(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0, double& acc,
@@ -249,28 +276,7 @@ __device__ __forceinline__ void do_vec(const Ctx& x, const Scal& k, const AdamSc
         st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
         st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
     }
-    if constexpr (OP == Op::Full || OP == Op::Adam) {
-        const f32x4 w0 = ld4(x.master + e0), w1 = ld4(x.master + e0 + 4);
-        const f32x4 m0 = ld4(x.m + e0), m1 = ld4(x.m + e0 + 4);
-        const f32x4 v0 = ld4(x.v + e0), v1 = ld4(x.v + e0 + 4);
-        float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) adam1(g[j], k.coef, c, w[j], m[j], v[j]);
-        st4(x.master + e0, f32x4{w[0], w[1], w[2], w[3]});
-        st4(x.master + e0 + 4, f32x4{w[4], w[5], w[6], w[7]});
-        st4(x.m + e0, f32x4{m[0], m[1], m[2], m[3]});
-        st4(x.m + e0 + 4, f32x4{m[4], m[5], m[6], m[7]});
-        st4(x.v + e0, f32x4{v[0], v[1], v[2], v[3]});
-        st4(x.v + e0 + 4, f32x4{v[4], v[5], v[6], v[7]});
-        u32x4 o;
-        o.x = bf16_rne(w[0]) | (bf16_rne(w[1]) << 16);
-        o.y = bf16_rne(w[2]) | (bf16_rne(w[3]) << 16);
-        o.z = bf16_rne(w[4]) | (bf16_rne(w[5]) << 16);
-        o.w = bf16_rne(w[6]) | (bf16_rne(w[7]) << 16);
-        st_nt(x.out + e0, o);
-    }
+    if constexpr (OP == Op::Full || OP == Op::Adam) adam8(x, k, c, e0, g);
 }
 
 // Tile `t` of one shard.
@@ -292,6 +298,89 @@ __device__ __forceinline__ void do_tile(const Ctx& x, const Scal& k, const AdamS
             if (e < x.n) do_one<OP, MT, FROM0>(x, k, c, e, acc, bad);
         }
     }
+}
+
+// Tile `t` of one shard in the fused kernels' geometry (NT threads, U
+// vectors per thread). The fold sweeps the replicas in ascending rank order
+// with a workgroup barrier after each replica, so the workgroup requests
+// NT*U*16 contiguous bytes of one replica together: long runs per DRAM page
+// with 64+ concurrent replica streams.
+template <Op OP, int NT, int U>
+__device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t t, double& acc,
+                                         uint32_t& bad)
+{
+    const int tid = threadIdx.x;
+    constexpr int64_t kTileVecs = static_cast<int64_t>(NT) * U;
+    if (x.nvec < 0) {  // scalar layout: element by element
+        const int64_t base = t * kTileVecs * kVec;
+        for (int j = 0; j < U * kVec; ++j) {
+            const int64_t e = base + static_cast<int64_t>(j) * NT + tid;
+            if (e < x.n) do_one<OP, 0, true>(x, k, c, e, acc, bad);
+        }
+        return;
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t v0 = t * kTileVecs + static_cast<int64_t>(wave) * 64 * U + lane;
+    if constexpr (OP == Op::Full || OP == Op::PassA) {
+        bool ok[U];
+        float s[U][8];
+        const uint16_t* p0 = x.gp[0] + x.head;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            ok[u] = v0 + u * 64 < x.nvec;
+            if (ok[u]) {
+                set8(s[u], ld_nt(p0 + (v0 + u * 64) * kVec));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) s[u][j] = 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int r = 1; r < x.M; ++r) {
+            const uint16_t* p = x.gp[r] + x.head;
+            u32x4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = ok[u] ? ld_nt(p + (v0 + u * 64) * kVec) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < U; ++u) add8(s[u], w[u]);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!ok[u]) continue;
+            const int64_t e0 = x.head + (v0 + u * 64) * kVec;
+            float g[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                g[j] = s[u][j] * k.gscale;
+                bad |= nonfinite(g[j]);
+                const double d = static_cast<double>(g[j]);
+                acc = fma(d, d, acc);
+            }
+            if constexpr (OP == Op::PassA) {
+                st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
+                st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
+            } else {
+                adam8(x, k, c, e0, g);
+            }
+        }
+    } else {
+        static_assert(OP == Op::Adam, "fused tiles fold, or update from the stored gradient");
+#pragma unroll 1
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + u * 64;
+            if (v < x.nvec) {
+                const int64_t e0 = x.head + v * kVec;
+                const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
+                const float g[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                adam8(x, k, c, e0, g);
+            }
+        }
+    }
+    if (t == 0 && tid < x.head) do_one<OP, 0, true>(x, k, c, tid, acc, bad);
+    const int64_t last = x.nvec > 0 ? (x.nvec - 1) / kTileVecs : 0;
+    if (t == last && tid < x.tail) do_one<OP, 0, true>(x, k, c, x.head + x.nvec * kVec + tid, acc, bad);
 }
 
 __device__ __forceinline__ Ctx ctx_of(const TensorDesc& d, int M)
@@ -378,13 +467,12 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Adam, 1, true>(x, k, c, t, acc, bad);
 }
 
-template <Mode MODE, int MT>
-__global__ __launch_bounds__(kThreads) void fused_kernel(const PlanHeader* __restrict__ hdr,
-                                                         const TensorDesc* __restrict__ desc,
-                                                         const TileRef* __restrict__ tiles, int64_t total_tiles,
-                                                         uint64_t sig, int M, float gscale, AdamScalars c,
-                                                         Partial* __restrict__ parts,
-                                                         const zero_result* __restrict__ res)
+template <Mode MODE, int NT, int U>
+__global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict__ hdr,
+                                                   const TensorDesc* __restrict__ desc,
+                                                   const TileRef* __restrict__ tiles, int64_t total_tiles,
+                                                   uint64_t sig, int M, float gscale, AdamScalars c,
+                                                   Partial* __restrict__ parts, const zero_result* __restrict__ res)
 {
     if (hdr->signature != sig) return;  // the workspace no longer holds this plan: write nothing
     float coef = 1.0f;
@@ -399,9 +487,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const PlanHeader* __res
     for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
         const TileRef tr = tiles[t];
         const Ctx x = ctx_of(desc[tr.tensor], M);
-        do_tile<OP, MT, true>(x, k, c, tr.local, acc, bad);
+        big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
     }
-    if constexpr (MODE != Mode::PassB) block_partial(acc, bad, parts + blockIdx.x);
+    if constexpr (MODE != Mode::PassB) block_partial<NT>(acc, bad, parts + blockIdx.x);
 }
 
 // One workgroup: combine the partials in index order, then the norm, the
@@ -492,7 +580,7 @@ int device_cus()
 // Resident workgroups of one kernel on the current device, cached per
 // (kernel, device).
 template <typename K>
-int resident(K kernel)
+int resident(K kernel, int block = kThreads)
 {
     static std::mutex mu;
     static std::map<std::pair<const void*, int>, int> cache;
@@ -505,7 +593,7 @@ int resident(K kernel)
         if (it != cache.end()) return it->second;
     }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu <= 0)
         per_cu = 1;
     int g = per_cu * device_cus();
     g = g < kMaxPartials ? g : kMaxPartials;
@@ -531,48 +619,35 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
     return hipGetLastError();
 }
 
+#define ZERO_FOR_EACH_GEOM(X) X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8)
+
 template <Mode MODE>
-hipError_t fused_dispatch(const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles, int64_t total_tiles,
-                          uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
+hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
+                          int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
                           const zero_result* res, int grid, hipStream_t s)
 {
-#define ZERO_FUSED(MTV)                                                                                       \
-    fused_kernel<MODE, MTV><<<grid, kThreads, 0, s>>>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, \
-                                                      res)
-    if constexpr (MODE == Mode::PassB) {
-        ZERO_FUSED(1);
-    } else {
-        switch (M) {
-        case 1: ZERO_FUSED(1); break;
-        case 2: ZERO_FUSED(2); break;
-        case 4: ZERO_FUSED(4); break;
-        case 8: ZERO_FUSED(8); break;
-        case 16: ZERO_FUSED(16); break;
-        case 32: ZERO_FUSED(32); break;
-        case 64: ZERO_FUSED(64); break;
-        default: ZERO_FUSED(0); break;
-        }
+    switch (geom) {
+#define ZERO_CASE(I, NTV, UV)                                                                                     \
+    case I:                                                                                                       \
+        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, \
+                                                         res);                                                    \
+        break;
+        ZERO_FOR_EACH_GEOM(ZERO_CASE)
+#undef ZERO_CASE
+    default: return hipErrorInvalidValue;
     }
-#undef ZERO_FUSED
     return hipGetLastError();
 }
 
 template <Mode MODE>
-int fused_resident(int M)
+int fused_resident(int geom)
 {
-    if constexpr (MODE == Mode::PassB) {
-        return resident(fused_kernel<MODE, 1>);
-    } else {
-        switch (M) {
-        case 1: return resident(fused_kernel<MODE, 1>);
-        case 2: return resident(fused_kernel<MODE, 2>);
-        case 4: return resident(fused_kernel<MODE, 4>);
-        case 8: return resident(fused_kernel<MODE, 8>);
-        case 16: return resident(fused_kernel<MODE, 16>);
-        case 32: return resident(fused_kernel<MODE, 32>);
-        case 64: return resident(fused_kernel<MODE, 64>);
-        default: return resident(fused_kernel<MODE, 0>);
-        }
+    switch (geom) {
+#define ZERO_CASE(I, NTV, UV) \
+    case I: return resident(fused_kernel<MODE, NTV, UV>, NTV);
+        ZERO_FOR_EACH_GEOM(ZERO_CASE)
+#undef ZERO_CASE
+    default: return 1;
     }
 }
 
@@ -620,17 +695,19 @@ hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_fused(Mode mode, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
+hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
                         int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
                         Partial* parts, const zero_result* res, int grid, hipStream_t s)
 {
     switch (mode) {
     case Mode::Full:
-        return fused_dispatch<Mode::Full>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+        return fused_dispatch<Mode::Full>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
     case Mode::PassA:
-        return fused_dispatch<Mode::PassA>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+        return fused_dispatch<Mode::PassA>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid,
+                                           s);
     case Mode::PassB:
-        return fused_dispatch<Mode::PassB>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
+        return fused_dispatch<Mode::PassB>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid,
+                                           s);
     }
     return hipErrorInvalidValue;
 }
@@ -645,14 +722,16 @@ int resident_grid_reduce(int Mc, bool first)
 int resident_grid_check() { return resident(check_kernel); }
 int resident_grid_adamw() { return resident(adamw_kernel); }
 
-int resident_grid_fused(Mode mode, int M)
+int resident_grid_fused(Mode mode, int geom)
 {
     switch (mode) {
-    case Mode::Full: return fused_resident<Mode::Full>(M);
-    case Mode::PassA: return fused_resident<Mode::PassA>(M);
-    case Mode::PassB: return fused_resident<Mode::PassB>(M);
+    case Mode::Full: return fused_resident<Mode::Full>(geom);
+    case Mode::PassA: return fused_resident<Mode::PassA>(geom);
+    case Mode::PassB: return fused_resident<Mode::PassB>(geom);
     }
     return 1;
 }
+
+int compute_units() { return device_cus(); }
 
 }  // namespace zero
