@@ -160,20 +160,17 @@ def main():
     if r["status"] != 0:
         raise RuntimeError(f"step status {r}")
     K = a.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps, on the stream the kernels run on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
-    t_begin.record(stream)
+    ev[0].record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(a.warmup + i)
-        ev[i][1].record(stream)
-    t_end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per_ms = sorted(s.elapsed_time(e) for s, e in ev)
-    avg_ms = sum(per_ms) / K
+    total_ms = ev[0].elapsed_time(ev[K])
+    per_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
+    avg_ms = total_ms / K
     n = w.n_total
     bpp = w.bytes_per_param()
     achieved = bpp * n / (avg_ms * 1e-3) / 1e9

@@ -1,0 +1,155 @@
+"""rocprofv3 evidence for bench.py: kernel trace + stats of the timed command,
+HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter passes (one
+counter per run), calibrated on a plain device copy of known size.
+
+    python bench_profile.py --workload 2 [--steps 10] [--out gpurun_out/prof]
+
+Runs on a GPU machine. Writes:
+  profiles/<kernel>_<workload tag>.md   the figures used and the commands that made them
+  profiles/traffic.json                 HBM bytes per launch of the dominant kernel, keyed by
+                                        workload and the hash of the kernel source (bench.py
+                                        reports it only while that hash is current)
+Raw rocprofv3 output stays under --out.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
+TAGS = {0: "tiny_n262144_M4", 1: "gpt2_bucket_n15554976_M8", 2: "7p5B_shard_n117187500_M64",
+        3: "llama7b_ragged_n809533440_M8", 4: "amp_shard_n2e9_M8"}
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def run(cmd, log):
+    print("+", " ".join(cmd), flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(cmd, stdout=f, stderr=subprocess.STDOUT, cwd=ROOT, timeout=600)
+    if r.returncode != 0:
+        sys.exit(f"command failed ({r.returncode}): {' '.join(cmd)}; see {log}")
+
+
+def one(pattern):
+    hits = glob.glob(pattern)
+    if len(hits) != 1:
+        sys.exit(f"expected one file for {pattern}, found {hits}")
+    return hits[0]
+
+
+def counter_per_dispatch(path, kernel_pred):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kernel_pred(r["Kernel_Name"])]
+    if not vals:
+        sys.exit(f"no matching dispatch in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--out", default=os.path.join("gpurun_out", "prof"), help="raw rocprofv3 output (relative)")
+    ap.add_argument("--profiles-dir", default="profiles", help="where the summaries go (relative)")
+    ap.add_argument("--summarize-only", action="store_true", help="re-read existing raw output, run nothing")
+    a = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    from synth.workloads import workload
+    w = workload(a.workload)
+    out = os.path.join(a.out, f"w{a.workload}")  # relative to the repository root
+    os.chdir(ROOT)
+    os.makedirs(out, exist_ok=True)
+    profiles = a.profiles_dir
+    bench = ["python", "-u", "bench.py", "--workload", str(a.workload), "--cpu-sample", "0", "--steps",
+             str(a.steps), "--warmup", "2"]
+    calib = ["python", "-u", "bench.py", "--calib-copy", "--steps", "3"]
+    rp = "rocprofv3"
+    cmds = {
+        "trace": [rp, "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace", "-o", "run",
+                  "--"] + bench,
+        "fetch": [rp, "--pmc", "FETCH_SIZE", "--output-format", "csv", "-d", f"{out}/fetch", "-o", "run", "--"] + bench,
+        "write": [rp, "--pmc", "WRITE_SIZE", "--output-format", "csv", "-d", f"{out}/write", "-o", "run", "--"] + bench,
+        "cfetch": [rp, "--pmc", "FETCH_SIZE", "--output-format", "csv", "-d", f"{out}/cfetch", "-o", "run", "--"] + calib,
+        "cwrite": [rp, "--pmc", "WRITE_SIZE", "--output-format", "csv", "-d", f"{out}/cwrite", "-o", "run", "--"] + calib,
+    }
+    if not a.summarize_only:
+        for k, c in cmds.items():
+            run(c, f"{out}/{k}.log")
+
+    stats = list(csv.DictReader(open(one(f"{out}/trace/run_kernel_stats.csv"))))
+    ours = [r for r in stats if "fused_kernel" in r["Name"] or "finalize_kernel" in r["Name"]
+            or "partials_kernel" in r["Name"]]
+    dom = max((r for r in ours if "fused_kernel" in r["Name"]), key=lambda r: float(r["TotalDurationNs"]))
+    dom_name = dom["Name"]
+    is_dom = lambda name: name == dom_name
+    copy_name = "__amd_rocclr_copyBuffer"
+    fetch_kib, nf = counter_per_dispatch(one(f"{out}/fetch/run_counter_collection.csv"), is_dom)
+    write_kib, nw = counter_per_dispatch(one(f"{out}/write/run_counter_collection.csv"), is_dom)
+    cf_kib, _ = counter_per_dispatch(one(f"{out}/cfetch/run_counter_collection.csv"), lambda n: n == copy_name)
+    cw_kib, _ = counter_per_dispatch(one(f"{out}/cwrite/run_counter_collection.csv"), lambda n: n == copy_name)
+    copy_bytes = 4 << 30
+    f_fetch = cf_kib * 1024 / copy_bytes
+    f_write = cw_kib * 1024 / copy_bytes
+    fetch_b = fetch_kib * 1024 / f_fetch
+    write_b = write_kib * 1024 / f_write
+    n = w.n_total
+    # bytes of the dominant kernel by the traffic model: single pass 2M+26, or the
+    # fold pass (2M+4) / update pass (30) of a two-pass step
+    if not w.two_pass:
+        alg = (2 * w.M + 26) * n
+    elif "(zero::Mode)1" in dom_name:
+        alg = (2 * w.M + 4) * n
+    else:
+        alg = 30 * n
+    avg_us = float(dom["AverageNs"]) / 1e3
+    achieved = alg / (avg_us * 1e-6) / 1e9
+    kshort = dom_name.split("(zero::PlanHeader")[0].replace("void zero::(anonymous namespace)::", "")
+    kfile = kshort.replace("<(zero::Mode)", "_mode").replace(", ", "_").replace(">", "").replace("<", "_")
+    os.makedirs(profiles, exist_ok=True)
+    md = os.path.join(profiles, f"{kfile}_{TAGS[a.workload]}.md")
+    with open(md, "w") as f:
+        f.write(f"# {kshort} on {w.name}\n\n")
+        f.write("Commands (repository root, MI355X, ROCm 7.2):\n\n")
+        for k, c in cmds.items():
+            f.write(f"    {' '.join(c)}\n")
+        f.write("\nKernel stats (rocprofv3 --kernel-trace --stats), kernels of the step:\n\n")
+        f.write("| kernel | calls | average us | min us | max us |\n|---|---|---|---|---|\n")
+        for r in ours:
+            nm = r["Name"].replace("void zero::(anonymous namespace)::", "").replace("zero::(anonymous namespace)::", "")
+            nm = re.split(r"\((?:zero::PlanHeader|zero::Partial)", nm)[0]
+            f.write(f"| {nm} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {float(r['MinNs'])/1e3:.2f} | "
+                    f"{float(r['MaxNs'])/1e3:.2f} |\n")
+        f.write(f"\nDominant kernel: `{kshort}`, average {avg_us:.2f} us over {dom['Calls']} launches.\n")
+        f.write(f"Algorithmic bytes per launch: {alg:,.0f} ({alg / n:.0f} B x {n:,} parameters) -> "
+                f"{achieved:.1f} GB/s = {achieved / 8000:.4f} of 8000 GB/s.\n\n")
+        f.write("HBM counters per launch (average over dispatches), calibrated on a 4 GiB device copy:\n\n")
+        f.write(f"- copy calibration: FETCH_SIZE {cf_kib:,.1f} KiB and WRITE_SIZE {cw_kib:,.1f} KiB for "
+                f"{copy_bytes:,} B each -> factors {f_fetch:.4f} (read), {f_write:.4f} (write)\n")
+        f.write(f"- FETCH_SIZE {fetch_kib:,.1f} KiB over {nf} dispatches -> {fetch_b:,.0f} B read\n")
+        f.write(f"- WRITE_SIZE {write_kib:,.1f} KiB over {nw} dispatches -> {write_b:,.0f} B written\n")
+        f.write(f"- traffic {fetch_b + write_b:,.0f} B per launch = {(fetch_b + write_b) / alg:.4f} x the "
+                f"algorithmic bytes\n")
+        f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
+    tf_path = os.path.join(profiles, "traffic.json")
+    tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
+    tf[str(a.workload)] = {"kernel": kshort, "kernel_source_sha256_16": src_hash(),
+                           "bytes_per_launch": round(fetch_b + write_b), "read_bytes": round(fetch_b),
+                           "write_bytes": round(write_b), "algorithmic_bytes": alg,
+                           "rocprof_avg_us": round(avg_us, 2), "fetch_factor": round(f_fetch, 5),
+                           "write_factor": round(f_write, 5), "summary": os.path.join("profiles", os.path.basename(md))}
+    json.dump(tf, open(tf_path, "w"), indent=1, sort_keys=True)
+    print(open(md).read())
+
+
+if __name__ == "__main__":
+    main()

@@ -90,17 +90,34 @@ int grid_for(int64_t tiles, int resident)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ZERO_OK : ZERO_ERR_HIP; }
 
-// The fused kernels' geometry: the longest per-replica bursts (largest tile)
-// that still give every compute unit at least one tile; small buckets fall
-// back to 2048-element tiles.
-int pick_geom(const std::vector<Layout>& layouts, int cus)
+int64_t tiles_of(const std::vector<Layout>& layouts, int geom)
 {
-    for (int g = kNumGeoms - 1; g > 0; --g) {
-        const int64_t tv = static_cast<int64_t>(kGeoms[g].nt) * kGeoms[g].u;
-        int64_t tiles = 0;
-        for (const Layout& L : layouts) tiles += layout_tiles(L, tv);
-        if (tiles >= cus) return g;
-    }
+    const int64_t tv = static_cast<int64_t>(kGeoms[geom].nt) * kGeoms[geom].u;
+    int64_t tiles = 0;
+    for (const Layout& L : layouts) tiles += layout_tiles(L, tv);
+    return tiles;
+}
+
+// Geometry of the pass that folds the replicas. Long per-replica bursts
+// (the largest tile that still reaches half the compute units) pay off when
+// the replicas dominate the traffic: many ranks, or the first pass of a
+// two-pass step, which writes only the 4-byte reduced gradient. A single pass
+// over few ranks is dominated by the master/m/v read-modify-write, which
+// streams best in small tiles.
+int pick_geom_fold(const std::vector<Layout>& layouts, int M, bool two_pass, int cus)
+{
+    if (!two_pass && M < 16) return 0;
+    for (int g = kNumGeoms - 1; g > 0; --g)
+        if (2 * tiles_of(layouts, g) >= static_cast<int64_t>(cus)) return g;
+    return 0;
+}
+
+// Geometry of the update pass of a two-pass step (no replica streams):
+// small tiles, like any read-modify-write stream.
+int pick_geom_update(const std::vector<Layout>& layouts, int cus)
+{
+    (void)layouts;
+    (void)cus;
     return 0;
 }
 
@@ -109,17 +126,20 @@ int pick_geom(const std::vector<Layout>& layouts, int cus)
 PlanOffsets plan_offsets(const zero_tensor* ts, int32_t T, int32_t M, bool two_pass)
 {
     PlanOffsets o{};
-    int64_t tiles = 0;
+    int64_t tiles = 0;  // bound over every geometry (the smallest tile is kTileElems)
     size_t gbytes = 0;
     for (int32_t t = 0; t < T; ++t) {
         tiles += tiles_bound(ts[t].n);
         if (two_pass && ts[t].n > 0) gbytes += align_up((static_cast<size_t>(ts[t].n) + 3) * 4, kAlign);
     }
+    const size_t ntiles = static_cast<size_t>(tiles);
     o.desc = kAlign;
     o.ptrs = align_up(o.desc + sizeof(TensorDesc) * static_cast<size_t>(T), kAlign);
-    o.tiles = align_up(o.ptrs + sizeof(void*) * static_cast<size_t>(T) * static_cast<size_t>(M), kAlign);
-    o.parts = align_up(o.tiles + sizeof(TileRef) * static_cast<size_t>(tiles), kAlign);
-    o.gbuf = align_up(o.parts + sizeof(Partial) * static_cast<size_t>(kMaxPartials), kAlign);
+    o.map0 = align_up(o.ptrs + sizeof(void*) * static_cast<size_t>(T) * static_cast<size_t>(M), kAlign);
+    o.map1 = align_up(o.map0 + sizeof(TileRef) * ntiles, kAlign);
+    o.parts = align_up(o.map1 + (two_pass ? sizeof(TileRef) * ntiles : 0), kAlign);
+    o.parts1 = align_up(o.parts + sizeof(Partial) * ntiles, kAlign);
+    o.gbuf = align_up(o.parts1 + sizeof(Partial) * ((ntiles + kFinalizeChunk - 1) / kFinalizeChunk), kAlign);
     o.total = o.gbuf + gbytes;
     return o;
 }
@@ -202,7 +222,7 @@ int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp
     const double max_norm = hp ? hp->max_grad_norm : 0.0;
     const int skip = hp ? (hp->skip_on_nonfinite != 0) : 0;
     if (n == 0)
-        return hip_status(launch_finalize(nullptr, 0, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+        return hip_status(launch_finalize(nullptr, 0, nullptr, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
     if (g == nullptr || ws == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(ws) % 16u != 0) return ZERO_ERR_INVALID_ARGUMENT;
     if (ws_bytes < zero_grad_check_norm_workspace_bytes(n)) return ZERO_ERR_WORKSPACE_TOO_SMALL;
@@ -212,7 +232,7 @@ int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp
     Partial* parts = static_cast<Partial*>(ws);
     hipError_t e = launch_check(g, L, parts, grid, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
-    return hip_status(launch_finalize(parts, grid, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+    return hip_status(launch_finalize(parts, grid, nullptr, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
 }
 
 int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out, int64_t n,
@@ -259,14 +279,15 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     const int skip = hp->skip_on_nonfinite != 0;
     if (total_n == 0)
         return hip_status(
-            launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, nullptr, 0, stream));
+            launch_finalize(nullptr, 0, nullptr, external_sumsq, hp->max_grad_norm, skip, res_dev, nullptr, 0,
+                            stream));
     if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
     const PlanOffsets off = plan_offsets(tensors, T, M, two_pass);
     if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
 
     // ---- the plan: header, tensor table, rank-pointer table (host image)
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    std::vector<uint8_t> blob(off.tiles, 0);
+    std::vector<uint8_t> blob(off.map0, 0);
     PlanHeader* hdr = reinterpret_cast<PlanHeader*>(blob.data());
     TensorDesc* desc = reinterpret_cast<TensorDesc*>(blob.data() + off.desc);
     const uint16_t** ptrs = reinterpret_cast<const uint16_t**>(blob.data() + off.ptrs);
@@ -286,19 +307,20 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
-    const int geom = pick_geom(layouts, compute_units());
-    const int64_t tile_vecs = static_cast<int64_t>(kGeoms[geom].nt) * kGeoms[geom].u;
-    int64_t tile = 0;
+    const int cus = compute_units();
+    const int geom[2] = {pick_geom_fold(layouts, M, two_pass, cus), two_pass ? pick_geom_update(layouts, cus) : 0};
+    const int64_t tile_vecs[2] = {static_cast<int64_t>(kGeoms[geom[0]].nt) * kGeoms[geom[0]].u,
+                                  static_cast<int64_t>(kGeoms[geom[1]].nt) * kGeoms[geom[1]].u};
+    int64_t tiles[2] = {0, 0};
     size_t gpos = off.gbuf;
     for (int32_t t = 0; t < T; ++t) {
         const zero_tensor& x = tensors[t];
         TensorDesc& d = desc[t];
         d.grads = reinterpret_cast<const uint16_t* const*>(wsb + off.ptrs + sizeof(void*) * static_cast<size_t>(t) * M);
         d.n = x.n;
-        d.tile_begin = tile;
+        for (int p = 0; p < 2; ++p) d.tile_begin[p] = tiles[p];
         if (x.n == 0) {
             d.nvec = -1;
-            d.ntiles = 0;
             continue;
         }
         for (int32_t r = 0; r < M; ++r)
@@ -311,23 +333,23 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
         d.nvec = L.nvec;
         d.head = L.head;
         d.tail = L.tail;
-        d.ntiles = layout_tiles(L, tile_vecs);
+        d.ntiles[0] = layout_tiles(L, tile_vecs[0]);
+        d.ntiles[1] = two_pass ? layout_tiles(L, tile_vecs[1]) : 0;
         if (two_pass) {
             // aligned with the other pointers at element `head`
             const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
             d.gbuf = reinterpret_cast<float*>(wsb + gpos + shift);
             gpos += align_up((static_cast<size_t>(x.n) + 3) * 4, kAlign);
         }
-        tile += d.ntiles;
+        for (int p = 0; p < 2; ++p) tiles[p] += d.ntiles[p];
     }
-    const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
-    const int grid = grid_for(tile, resident_grid_fused(first_mode, geom));
-    hdr->total_tiles = tile;
+    hdr->tiles[0] = tiles[0];
+    hdr->tiles[1] = tiles[1];
     hdr->T = T;
     hdr->M = M;
-    hdr->grid = grid;
+    hdr->geom[0] = geom[0];
+    hdr->geom[1] = geom[1];
     hdr->two_pass = two_pass ? 1 : 0;
-    hdr->geom = geom;
     uint64_t sig = fnv1a(blob.data(), blob.size(), 1469598103934665603ull);
     const uintptr_t wsaddr = reinterpret_cast<uintptr_t>(ws);
     sig = fnv1a(reinterpret_cast<const uint8_t*>(&wsaddr), sizeof(wsaddr), sig);
@@ -343,10 +365,12 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     }
     PlanHeader* hdr_dev = reinterpret_cast<PlanHeader*>(wsb);
     TensorDesc* desc_dev = reinterpret_cast<TensorDesc*>(wsb + off.desc);
-    TileRef* tiles_dev = reinterpret_cast<TileRef*>(wsb + off.tiles);
-    Partial* parts_dev = reinterpret_cast<Partial*>(wsb + off.parts);
+    TileRef* map0 = reinterpret_cast<TileRef*>(wsb + off.map0);
+    TileRef* map1 = two_pass ? reinterpret_cast<TileRef*>(wsb + off.map1) : nullptr;
+    Partial* parts = reinterpret_cast<Partial*>(wsb + off.parts);
+    Partial* parts1 = reinterpret_cast<Partial*>(wsb + off.parts1);
     if (!cached) {
-        // tables first, tile map next, header (with the signature) last
+        // tables first, tile maps next, header (with the signature) last
         WriteChunk c;
         const size_t bytes_per = sizeof(c.data);
         for (size_t pos = off.desc; pos < blob.size(); pos += bytes_per) {
@@ -357,7 +381,7 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
             std::memcpy(c.data, blob.data() + pos, len);
             if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
         }
-        if (launch_plan_tiles(desc_dev, T, tiles_dev, stream) != hipSuccess) return ZERO_ERR_HIP;
+        if (launch_plan_tiles(desc_dev, T, map0, map1, stream) != hipSuccess) return ZERO_ERR_HIP;
         c.offset = 0;
         c.words = static_cast<uint32_t>(off.desc / 4);
         c.pad = 0;
@@ -370,15 +394,15 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     // ---- the step
     const AdamScalars c = derive(hp);
     const float gscale = static_cast<float>(hp->grad_scale);
-    hipError_t e = launch_fused(first_mode, geom, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev,
-                                nullptr, grid, stream);
+    const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
+    hipError_t e = launch_fused(first_mode, geom[0], hdr_dev, desc_dev, map0, tiles[0], sig, M, gscale, c, parts,
+                                nullptr, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
-    e = launch_finalize(parts_dev, grid, external_sumsq, hp->max_grad_norm, skip, res_dev, hdr_dev, sig, stream);
+    e = launch_finalize(parts, tiles[0], parts1, external_sumsq, hp->max_grad_norm, skip, res_dev, hdr_dev, sig, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
     if (two_pass) {
-        const int grid_b = grid_for(tile, resident_grid_fused(Mode::PassB, geom));
-        e = launch_fused(Mode::PassB, geom, hdr_dev, desc_dev, tiles_dev, tile, sig, M, gscale, c, parts_dev, res_dev,
-                         grid_b, stream);
+        e = launch_fused(Mode::PassB, geom[1], hdr_dev, desc_dev, map1, tiles[1], sig, M, gscale, c, parts, res_dev,
+                         stream);
         if (e != hipSuccess) return ZERO_ERR_HIP;
     }
     return ZERO_OK;

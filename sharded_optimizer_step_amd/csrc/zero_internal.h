@@ -80,10 +80,10 @@ struct alignas(16) TensorDesc {
     int64_t nvec;
     int32_t head;
     int32_t tail;
-    int64_t tile_begin;            // first global tile of this tensor
-    int64_t ntiles;
+    int64_t tile_begin[2];         // first tile of this tensor in the fold-pass / update-pass maps
+    int64_t ntiles[2];
 };
-static_assert(sizeof(TensorDesc) == 96, "TensorDesc layout");
+static_assert(sizeof(TensorDesc) == 112, "TensorDesc layout");
 
 struct TileRef {
     int32_t tensor;
@@ -96,20 +96,22 @@ struct alignas(16) Partial {
     uint32_t pad;
 };
 
+// Partials combined per workgroup by the first level of a two-level finalize.
+constexpr int kFinalizeChunk = 4096;
+
 struct alignas(16) PlanHeader {
     uint64_t signature;
-    int64_t total_tiles;
+    int64_t tiles[2];  // tiles of the fold pass (one partial each) and of the update pass
     int32_t T;
     int32_t M;
-    int32_t grid;
+    int32_t geom[2];   // kGeoms index of each pass
     int32_t two_pass;
-    int32_t geom;  // index into kGeoms
     int32_t pad;
 };
 
 // Byte offsets of the regions of a zero_step workspace.
 struct PlanOffsets {
-    size_t desc, ptrs, tiles, parts, gbuf, total;
+    size_t desc, ptrs, map0, map1, parts, parts1, gbuf, total;
 };
 
 // Payload of one plan-upload launch (carried in the kernel arguments).
@@ -139,20 +141,23 @@ hipError_t launch_reduce(const RankPtrs& ptrs, int Mc, bool first, bool last, fl
 hipError_t launch_check(const float* g, const Layout& L, Partial* parts, int grid, hipStream_t s);
 hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint16_t* out, const Layout& L,
                         const AdamScalars& c, const zero_result* res, int grid, hipStream_t s);
-hipError_t launch_finalize(const Partial* parts, int nparts, double external, double max_norm, int skip,
-                           zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s);
+// Norm/flag finalize over nparts partials into the result record; when
+// nparts > kFinalizeChunk and `level1` is given, a first launch combines
+// chunks of kFinalizeChunk partials into `level1`.
+hipError_t launch_finalize(const Partial* parts, int64_t nparts, Partial* level1, double external, double max_norm,
+                           int skip, zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s);
 hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s);
-hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipStream_t s);
-hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
-                        int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
-                        Partial* parts, const zero_result* res, int grid, hipStream_t s);
+hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* map0, TileRef* map1, hipStream_t s);
+// One workgroup per tile: grid = tiles of the pass.
+hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map,
+                        int64_t tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
+                        const zero_result* res, hipStream_t s);
 
 // Workgroups of 256 threads that one kernel keeps resident on the current
 // device (occupancy x compute units), for the grid-stride launches.
 int resident_grid_reduce(int Mc, bool first);
 int resident_grid_check();
 int resident_grid_adamw();
-int resident_grid_fused(Mode mode, int geom);
 int compute_units();  // of the current device
 
 }  // namespace zero

@@ -467,12 +467,16 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Adam, 1, true>(x, k, c, t, acc, bad);
 }
 
+// One workgroup per tile (grid = tiles): the workgroups in flight cover a
+// compact window of the buffers that advances as the dispatcher hands out
+// tiles in order, and the partial of tile t is written to parts[t] whatever
+// the order in which tiles run.
 template <Mode MODE, int NT, int U>
 __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict__ hdr,
                                                    const TensorDesc* __restrict__ desc,
-                                                   const TileRef* __restrict__ tiles, int64_t total_tiles,
-                                                   uint64_t sig, int M, float gscale, AdamScalars c,
-                                                   Partial* __restrict__ parts, const zero_result* __restrict__ res)
+                                                   const TileRef* __restrict__ map, uint64_t sig, int M, float gscale,
+                                                   AdamScalars c, Partial* __restrict__ parts,
+                                                   const zero_result* __restrict__ res)
 {
     if (hdr->signature != sig) return;  // the workspace no longer holds this plan: write nothing
     float coef = 1.0f;
@@ -484,17 +488,31 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
     const Scal k{gscale, coef, false};
     double acc = 0.0;
     uint32_t bad = 0;
-    for (int64_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-        const TileRef tr = tiles[t];
-        const Ctx x = ctx_of(desc[tr.tensor], M);
-        big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
-    }
+    const TileRef tr = map[blockIdx.x];
+    const Ctx x = ctx_of(desc[tr.tensor], M);
+    big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
     if constexpr (MODE != Mode::PassB) block_partial<NT>(acc, bad, parts + blockIdx.x);
+}
+
+// First level of a two-level finalize: workgroup w combines partials
+// [w*C, min(n, (w+1)*C)) in a fixed order.
+__global__ __launch_bounds__(kThreads) void partials_kernel(const Partial* __restrict__ parts, int64_t nparts,
+                                                            Partial* __restrict__ out)
+{
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kFinalizeChunk;
+    const int64_t e = b + kFinalizeChunk < nparts ? b + kFinalizeChunk : nparts;
+    double acc = 0.0;
+    uint32_t bad = 0;
+    for (int64_t i = b + threadIdx.x; i < e; i += kThreads) {
+        acc += parts[i].sumsq;
+        bad |= parts[i].bad;
+    }
+    block_partial(acc, bad, out + blockIdx.x);
 }
 
 // One workgroup: combine the partials in index order, then the norm, the
 // clip coefficient and the skip decision.
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __restrict__ parts, int nparts,
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __restrict__ parts, int64_t nparts,
                                                             double external, double max_norm, int skip,
                                                             zero_result* __restrict__ res,
                                                             const PlanHeader* __restrict__ hdr, uint64_t sig)
@@ -515,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
     }
     double acc = 0.0;
     uint32_t bad = 0;
-    for (int i = threadIdx.x; i < nparts; i += kThreads) {
+    for (int64_t i = threadIdx.x; i < nparts; i += kThreads) {
         acc += parts[i].sumsq;
         bad |= parts[i].bad;
     }
@@ -549,15 +567,19 @@ __global__ __launch_bounds__(kThreads) void plan_write_kernel(uint8_t* __restric
 }
 
 __global__ __launch_bounds__(kThreads) void plan_tiles_kernel(const TensorDesc* __restrict__ desc, int T,
-                                                              TileRef* __restrict__ tiles)
+                                                              TileRef* __restrict__ map0, TileRef* __restrict__ map1)
 {
     for (int t = blockIdx.x; t < T; t += gridDim.x) {
-        const int64_t b = desc[t].tile_begin, nt = desc[t].ntiles;
-        for (int64_t j = threadIdx.x; j < nt; j += kThreads) {
-            TileRef r;
-            r.tensor = t;
-            r.local = static_cast<int32_t>(j);
-            tiles[b + j] = r;
+        for (int p = 0; p < 2; ++p) {
+            TileRef* map = p == 0 ? map0 : map1;
+            if (map == nullptr) continue;
+            const int64_t b = desc[t].tile_begin[p], nt = desc[t].ntiles[p];
+            for (int64_t j = threadIdx.x; j < nt; j += kThreads) {
+                TileRef r;
+                r.tensor = t;
+                r.local = static_cast<int32_t>(j);
+                map[b + j] = r;
+            }
         }
     }
 }
@@ -622,33 +644,22 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
 #define ZERO_FOR_EACH_GEOM(X) X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8)
 
 template <Mode MODE>
-hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
-                          int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
-                          const zero_result* res, int grid, hipStream_t s)
+hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map, int64_t tiles,
+                          uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
+                          const zero_result* res, hipStream_t s)
 {
+    if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned grid = static_cast<unsigned>(tiles);
     switch (geom) {
-#define ZERO_CASE(I, NTV, UV)                                                                                     \
-    case I:                                                                                                       \
-        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, \
-                                                         res);                                                    \
+#define ZERO_CASE(I, NTV, UV)                                                                          \
+    case I:                                                                                            \
+        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, map, sig, M, gscale, c, parts, res); \
         break;
         ZERO_FOR_EACH_GEOM(ZERO_CASE)
 #undef ZERO_CASE
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
-}
-
-template <Mode MODE>
-int fused_resident(int geom)
-{
-    switch (geom) {
-#define ZERO_CASE(I, NTV, UV) \
-    case I: return resident(fused_kernel<MODE, NTV, UV>, NTV);
-        ZERO_FOR_EACH_GEOM(ZERO_CASE)
-#undef ZERO_CASE
-    default: return 1;
-    }
 }
 
 }  // namespace
@@ -675,9 +686,17 @@ hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint1
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const Partial* parts, int nparts, double external, double max_norm, int skip,
-                           zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s)
+hipError_t launch_finalize(const Partial* parts, int64_t nparts, Partial* level1, double external, double max_norm,
+                           int skip, zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s)
 {
+    if (nparts > kFinalizeChunk && level1 != nullptr) {
+        const int64_t g1 = (nparts + kFinalizeChunk - 1) / kFinalizeChunk;
+        partials_kernel<<<static_cast<unsigned>(g1), kThreads, 0, s>>>(parts, nparts, level1);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        parts = level1;
+        nparts = g1;
+    }
     finalize_kernel<<<1, kThreads, 0, s>>>(parts, nparts, external, max_norm, skip, res, hdr, sig);
     return hipGetLastError();
 }
@@ -688,26 +707,21 @@ hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* tiles, hipStream_t s)
+hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* map0, TileRef* map1, hipStream_t s)
 {
     const int grid = T < 4096 ? (T > 0 ? T : 1) : 4096;
-    plan_tiles_kernel<<<grid, kThreads, 0, s>>>(desc, T, tiles);
+    plan_tiles_kernel<<<grid, kThreads, 0, s>>>(desc, T, map0, map1);
     return hipGetLastError();
 }
 
-hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* tiles,
-                        int64_t total_tiles, uint64_t sig, int M, float gscale, const AdamScalars& c,
-                        Partial* parts, const zero_result* res, int grid, hipStream_t s)
+hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map,
+                        int64_t tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
+                        const zero_result* res, hipStream_t s)
 {
     switch (mode) {
-    case Mode::Full:
-        return fused_dispatch<Mode::Full>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid, s);
-    case Mode::PassA:
-        return fused_dispatch<Mode::PassA>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid,
-                                           s);
-    case Mode::PassB:
-        return fused_dispatch<Mode::PassB>(geom, hdr, desc, tiles, total_tiles, sig, M, gscale, c, parts, res, grid,
-                                           s);
+    case Mode::Full: return fused_dispatch<Mode::Full>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
+    case Mode::PassA: return fused_dispatch<Mode::PassA>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
+    case Mode::PassB: return fused_dispatch<Mode::PassB>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
     }
     return hipErrorInvalidValue;
 }
@@ -721,16 +735,6 @@ int resident_grid_reduce(int Mc, bool first)
 
 int resident_grid_check() { return resident(check_kernel); }
 int resident_grid_adamw() { return resident(adamw_kernel); }
-
-int resident_grid_fused(Mode mode, int geom)
-{
-    switch (mode) {
-    case Mode::Full: return fused_resident<Mode::Full>(geom);
-    case Mode::PassA: return fused_resident<Mode::PassA>(geom);
-    case Mode::PassB: return fused_resident<Mode::PassB>(geom);
-    }
-    return 1;
-}
 
 int compute_units() { return device_cus(); }
 
