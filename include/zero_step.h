@@ -19,9 +19,10 @@
  *   norm  = sqrt(sum of g[i]^2 + external_sumsq)        (binary64 partials)
  *   coef  = min(1, max_grad_norm / (norm + 1e-6)) if max_grad_norm > 0 else 1
  *   skip  = found_inf && skip_on_nonfinite      (a skipped step writes nothing)
- *   AdamW (bias-corrected, eps outside the root, decay scaled by lr):
+ *   AdamW (bias-corrected, eps outside the root, decay scaled by lr),
+ *   evaluated in binary64 from the fp32 state and rounded once on store:
  *     m   = b1*m + (1-b1)*(coef*g);   v = b2*v + (1-b2)*(coef*g)^2
- *     w   = w*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps)
+ *     w   = w*(1 - lr*wd) - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)
  *   out   = bf16 round-to-nearest-even of the new fp32 w (the all-gather payload)
  *
  * AMP unscaling (grad_scale = 1/S) and the inf/NaN skip follow the
@@ -102,12 +103,11 @@ typedef struct zero_tensor {
 /* Device-resident result record of a step, 32 bytes, written by the library. */
 typedef struct zero_result {
     double sumsq;      /* sum of g^2 over every element of the call, plus external_sumsq */
+    double clip_coef;  /* coefficient applied to g, binary64 (1 when clipping is off) */
     float grad_norm;   /* sqrt(sumsq) rounded to fp32 (inf/NaN when found_inf) */
-    float clip_coef;   /* coefficient applied to g (1 when clipping is off) */
     int32_t found_inf; /* 1 when any unscaled reduced gradient is inf or NaN */
     int32_t skipped;   /* 1 when the update was not applied */
     int32_t status;    /* ZERO_OK, or ZERO_ERR_STALE_WORKSPACE */
-    int32_t reserved;
 } zero_result;
 
 /*

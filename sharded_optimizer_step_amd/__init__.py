@@ -163,7 +163,7 @@ def new_result(device=None) -> torch.Tensor:
 def read_result(res: torch.Tensor) -> dict:
     """Copy the record to the host (synchronizes with its stream)."""
     b = bytes(res.cpu().numpy().tobytes())
-    sumsq, norm, coef, found_inf, skipped, status, _ = struct.unpack("<dffiiii", b)
+    sumsq, coef, norm, found_inf, skipped, status = struct.unpack("<ddfiii", b)
     return dict(sumsq=sumsq, grad_norm=norm, clip_coef=coef, found_inf=found_inf, skipped=skipped, status=status)
 
 

@@ -37,22 +37,20 @@ bool hparams_ok(const zero_adamw_hparams* hp)
     return true;
 }
 
-// The fp32 scalars of one step, from binary64 ("CS336 Lecture 7", memory
-// table: the update runs on fp32 master, m and v).
+// The binary64 scalars of one step.
 AdamScalars derive(const zero_adamw_hparams* hp)
 {
     const double t = static_cast<double>(hp->step);
-    const double bc1 = 1.0 - std::pow(hp->beta1, t);
-    const double bc2 = 1.0 - std::pow(hp->beta2, t);
     AdamScalars c;
-    c.b1 = static_cast<float>(hp->beta1);
-    c.omb1 = static_cast<float>(1.0 - hp->beta1);
-    c.b2 = static_cast<float>(hp->beta2);
-    c.omb2 = static_cast<float>(1.0 - hp->beta2);
-    c.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
-    c.step_size = static_cast<float>(hp->lr / bc1);
-    c.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
-    c.eps = static_cast<float>(hp->eps);
+    c.b1 = hp->beta1;
+    c.omb1 = 1.0 - hp->beta1;
+    c.b2 = hp->beta2;
+    c.omb2 = 1.0 - hp->beta2;
+    c.decay = 1.0 - hp->lr * hp->weight_decay;
+    c.lr = hp->lr;
+    c.bc1 = 1.0 - std::pow(hp->beta1, t);
+    c.bc2 = 1.0 - std::pow(hp->beta2, t);
+    c.eps = hp->eps;
     return c;
 }
 
@@ -98,16 +96,17 @@ int64_t tiles_of(const std::vector<Layout>& layouts, int geom)
     return tiles;
 }
 
-// Geometry of the pass that folds the replicas. Long per-replica bursts
-// (the largest tile that still reaches half the compute units) pay off when
-// the replicas dominate the traffic: many ranks, or the first pass of a
-// two-pass step, which writes only the 4-byte reduced gradient. A single pass
-// over few ranks is dominated by the master/m/v read-modify-write, which
-// streams best in small tiles.
+// Geometry of the pass that folds the replicas: long per-replica bursts in
+// workgroup lockstep -- 512 threads x 16 vectors (128 KiB of one replica per
+// workgroup, registers to spare for the binary64 update) for a single pass,
+// 1024 x 8 for the first pass of a two-pass step (no update, more waves) --
+// unless the bucket is too small to reach half the compute units.
 int pick_geom_fold(const std::vector<Layout>& layouts, int M, bool two_pass, int cus)
 {
-    if (!two_pass && M < 16) return 0;
-    for (int g = kNumGeoms - 1; g > 0; --g)
+    (void)M;
+    const int first = two_pass ? 4 : 5;
+    if (2 * tiles_of(layouts, first) >= static_cast<int64_t>(cus)) return first;
+    for (int g = 3; g > 0; --g)
         if (2 * tiles_of(layouts, g) >= static_cast<int64_t>(cus)) return g;
     return 0;
 }

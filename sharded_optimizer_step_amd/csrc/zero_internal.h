@@ -18,14 +18,13 @@ constexpr int kInlineRanks = 64;             // rank pointers passed by value pe
 constexpr int kMaxPartials = 8192;           // per-workgroup partial records of one launch
 constexpr size_t kAlign = 256;
 
-// fp32 scalars of one AdamW step, derived on the host in binary64 and
-// rounded once.
+// binary64 scalars of one AdamW step, derived on the host.
 struct AdamScalars {
-    float b1, omb1, b2, omb2;  // beta1, 1-beta1, beta2, 1-beta2
-    float decay;               // 1 - lr*weight_decay
-    float step_size;           // lr / (1 - beta1^t)
-    float inv_sqrt_bc2;        // 1 / sqrt(1 - beta2^t)
-    float eps;
+    double b1, omb1, b2, omb2;  // beta1, 1-beta1, beta2, 1-beta2
+    double decay;               // 1 - lr*weight_decay
+    double lr;
+    double bc1, bc2;            // 1 - beta1^t, 1 - beta2^t
+    double eps;
 };
 
 // How the elements of one shard are visited.
@@ -62,7 +61,7 @@ struct Geom {
     int nt;
     int u;
 };
-constexpr Geom kGeoms[] = {{256, 1}, {1024, 1}, {1024, 2}, {1024, 4}, {1024, 8}};
+constexpr Geom kGeoms[] = {{256, 1}, {1024, 1}, {1024, 2}, {1024, 4}, {1024, 8}, {512, 16}};
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 
 // Upper bound of layout_tiles over every alignment of an n-element shard.

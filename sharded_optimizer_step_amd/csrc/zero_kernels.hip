@@ -110,15 +110,22 @@ __device__ __forceinline__ float fold_one(const uint16_t* const* __restrict__ gp
     return s;
 }
 
-// One AdamW element in fp32 (bias-corrected, eps outside the root, decay
-// decoupled and scaled by lr).
-__device__ __forceinline__ void adam1(float g, float coef, const AdamScalars& c, float& w, float& m, float& v)
+// One AdamW element: bias-corrected, eps outside the root, decay decoupled
+// and scaled by lr. Evaluated in binary64 from the fp32 state and rounded
+// once on store; every operation is a separate IEEE binary64 operation
+// (no contraction), so the new state is what a binary64 evaluation of the
+// formula gives, also where w*(1 - lr*wd) and the Adam step nearly cancel.
+__device__ __forceinline__ void adam1(float g32, double coef, const AdamScalars& c, float& w, float& m, float& v)
 {
-    const float gc = g * coef;
-    m = fmaf(c.b1, m, c.omb1 * gc);
-    v = fmaf(c.b2, v, (c.omb2 * gc) * gc);
-    const float denom = fmaf(sqrtf(v), c.inv_sqrt_bc2, c.eps);
-    w = fmaf(w, c.decay, -(c.step_size * (m / denom)));
+    const double g = static_cast<double>(g32) * coef;
+    const double mn = c.b1 * static_cast<double>(m) + c.omb1 * g;
+    const double vn = c.b2 * static_cast<double>(v) + c.omb2 * g * g;
+    const double m_hat = mn / c.bc1;
+    const double v_hat = vn / c.bc2;
+    const double wn = static_cast<double>(w) * c.decay - c.lr * m_hat / (sqrt(v_hat) + c.eps);
+    m = static_cast<float>(mn);
+    v = static_cast<float>(vn);
+    w = static_cast<float>(wn);
 }
 
 // Per-workgroup reduction of (sum of squares, non-finite flag) in a fixed
@@ -175,7 +182,7 @@ struct Ctx {
 
 struct Scal {
     float gscale;  // multiplier of the fp32 sum (applied when `last`)
-    float coef;    // clip coefficient (Adam, Full)
+    double coef;   // clip coefficient (Adam, Full)
     bool last;     // Reduce: this pass ends the fold
 };
 
@@ -422,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RankPtrs ptrs, int Mc,
     x.M = Mc;
     x.gout = g_out;
     x.gin = g_out;
-    const Scal k{scale, 1.0f, last != 0};
+    const Scal k{scale, 1.0, last != 0};
     const AdamScalars c{};
     double acc = 0.0;
     uint32_t bad = 0;
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const float* __restrict
 {
     Ctx x = ctx_flat(L);
     x.gin = g;
-    const Scal k{1.0f, 1.0f, false};
+    const Scal k{1.0f, 1.0, false};
     const AdamScalars c{};
     double acc = 0.0;
     uint32_t bad = 0;
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
                                                          uint16_t* __restrict__ out, Layout L, AdamScalars c,
                                                          const zero_result* __restrict__ res)
 {
-    float coef = 1.0f;
+    double coef = 1.0;
     if (res != nullptr) {
         if (res->skipped != 0 || res->status != 0) return;
         coef = res->clip_coef;
@@ -479,7 +486,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
                                                    const zero_result* __restrict__ res)
 {
     if (hdr->signature != sig) return;  // the workspace no longer holds this plan: write nothing
-    float coef = 1.0f;
+    double coef = 1.0;
     if constexpr (MODE == Mode::PassB) {
         if (res->skipped != 0 || res->status != 0) return;
         coef = res->clip_coef;
@@ -522,11 +529,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
             zero_result r;
             r.sumsq = __builtin_nan("");
             r.grad_norm = __builtin_nanf("");
-            r.clip_coef = __builtin_nanf("");
+            r.clip_coef = __builtin_nan("");
             r.found_inf = 0;
             r.skipped = 1;
             r.status = ZERO_ERR_STALE_WORKSPACE;
-            r.reserved = 0;
             *res = r;
         }
         return;
@@ -551,11 +557,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
         zero_result r;
         r.sumsq = total;
         r.grad_norm = static_cast<float>(norm);
-        r.clip_coef = static_cast<float>(coef);
+        r.clip_coef = coef;
         r.found_inf = s_total.bad != 0 ? 1 : 0;
         r.skipped = (s_total.bad != 0 && skip != 0) ? 1 : 0;
         r.status = ZERO_OK;
-        r.reserved = 0;
         *res = r;
     }
 }
@@ -641,7 +646,7 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
     return hipGetLastError();
 }
 
-#define ZERO_FOR_EACH_GEOM(X) X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8)
+#define ZERO_FOR_EACH_GEOM(X) X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8) X(5, 512, 16)
 
 template <Mode MODE>
 hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map, int64_t tiles,

@@ -37,7 +37,7 @@ def _stale(lib, src):
 def build_host(force: bool = False) -> str:
     if force or _stale(_HOST_LIB, _HOST_SRC):
         tmp = _HOST_LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
                                "-o", tmp, _HOST_SRC, "-lm"])
         os.replace(tmp, _HOST_LIB)
     return _HOST_LIB

@@ -150,3 +150,62 @@ def run_step(dts: List[z.ZeroTensor], hp: z.HParams, external: float = 0.0, ws=N
     res = z.new_result()
     z.zero_step(dts, hp, external, ws, res)
     return z.read_result(res), ws
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def sample_indices(n: int, rng, k: int = 40_000) -> np.ndarray:
+    """Sorted unique indices: both ends, around 2048- and 65536-element tile
+    boundaries, and uniform random ones."""
+    parts = [np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n)]
+    for step in (2048, 65536):
+        b = np.arange(step, n, step * max(1, n // (step * 200)))
+        parts.append(np.clip(np.concatenate([b - 9, b - 1, b, b + 7]), 0, n - 1))
+    parts.append(rng.integers(0, n, k))
+    return np.unique(np.concatenate(parts).astype(np.int64))
+
+
+def host_inputs_at(w, spec, idx: np.ndarray):
+    """Host copies of the workload's inputs at shard-local indices idx."""
+    g = idx + spec.start
+    st = lambda k, r=0: synth.stream_id(k, spec.tensor_id, r)
+    grads = [synth.host_bf16_at(g, w.seed, st(synth.KIND_GRAD, r), w.grad_std) for r in range(w.M)]
+    master = synth.host_f32_at(g, w.seed, st(synth.KIND_MASTER), w.master_std)
+    m = synth.host_f32_at(g, w.seed, st(synth.KIND_EXP_AVG), w.m_std) if w.m_std else np.zeros(idx.size, np.float32)
+    v = synth.host_f32_at(g, w.seed, st(synth.KIND_EXP_AVG_SQ), w.v_std, absval=True) if w.v_std else \
+        np.zeros(idx.size, np.float32)
+    return grads, master, m, v
+
+
+def oracle_sumsq_streaming(w, slice_elems: int = 1 << 22, workers: int = 16, inject=()):
+    """The oracle's sum of squares and non-finite flag over the whole workload,
+    regenerating the inputs on the host slice by slice (bounded memory). Slice
+    partials are combined in index order. `inject` lists (tensor, rank, index)
+    elements set to +inf."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
+    for ti, spec in enumerate(w.tensors):
+        for s0 in range(0, spec.n, slice_elems):
+            jobs.append((ti, s0, min(spec.n, s0 + slice_elems)))
+    inj = {}
+    for (t, r, i) in inject:
+        inj.setdefault(t, []).append((r, i))
+
+    def one(job):
+        ti, s0, s1 = job
+        spec = w.tensors[ti]
+        grads = [synth.host_bf16(s1 - s0, w.seed, synth.stream_id(synth.KIND_GRAD, spec.tensor_id, r), w.grad_std,
+                                 start=spec.start + s0) for r in range(w.M)]
+        for r, i in inj.get(ti, []):
+            if s0 <= i < s1:
+                grads[r][i - s0] = 0x7F80
+        g = oracle.reduce(grads, w.grad_scale)
+        return oracle.check(g)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(one, jobs))
+    total, bad = 0.0, 0
+    for s, f in res:
+        total += s
+        bad |= f
+    return total, bad
