@@ -137,8 +137,7 @@ PlanOffsets plan_offsets(const zero_tensor* ts, int32_t T, int32_t M, bool two_p
     o.map0 = align_up(o.ptrs + sizeof(void*) * static_cast<size_t>(T) * static_cast<size_t>(M), kAlign);
     o.map1 = align_up(o.map0 + sizeof(TileRef) * ntiles, kAlign);
     o.parts = align_up(o.map1 + (two_pass ? sizeof(TileRef) * ntiles : 0), kAlign);
-    o.parts1 = align_up(o.parts + sizeof(Partial) * ntiles, kAlign);
-    o.gbuf = align_up(o.parts1 + sizeof(Partial) * ((ntiles + kFinalizeChunk - 1) / kFinalizeChunk), kAlign);
+    o.gbuf = align_up(o.parts + sizeof(Partial) * ntiles, kAlign);
     o.total = o.gbuf + gbytes;
     return o;
 }
@@ -221,7 +220,7 @@ int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp
     const double max_norm = hp ? hp->max_grad_norm : 0.0;
     const int skip = hp ? (hp->skip_on_nonfinite != 0) : 0;
     if (n == 0)
-        return hip_status(launch_finalize(nullptr, 0, nullptr, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+        return hip_status(launch_finalize(nullptr, 0, external_sumsq, max_norm, skip, res_dev, stream));
     if (g == nullptr || ws == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     if (reinterpret_cast<uintptr_t>(ws) % 16u != 0) return ZERO_ERR_INVALID_ARGUMENT;
     if (ws_bytes < zero_grad_check_norm_workspace_bytes(n)) return ZERO_ERR_WORKSPACE_TOO_SMALL;
@@ -231,7 +230,7 @@ int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp
     Partial* parts = static_cast<Partial*>(ws);
     hipError_t e = launch_check(g, L, parts, grid, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
-    return hip_status(launch_finalize(parts, grid, nullptr, external_sumsq, max_norm, skip, res_dev, nullptr, 0, stream));
+    return hip_status(launch_finalize(parts, grid, external_sumsq, max_norm, skip, res_dev, stream));
 }
 
 int zero_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out, int64_t n,
@@ -278,8 +277,7 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     const int skip = hp->skip_on_nonfinite != 0;
     if (total_n == 0)
         return hip_status(
-            launch_finalize(nullptr, 0, nullptr, external_sumsq, hp->max_grad_norm, skip, res_dev, nullptr, 0,
-                            stream));
+            launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, stream));
     if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
     const PlanOffsets off = plan_offsets(tensors, T, M, two_pass);
     if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
@@ -367,7 +365,6 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     TileRef* map0 = reinterpret_cast<TileRef*>(wsb + off.map0);
     TileRef* map1 = two_pass ? reinterpret_cast<TileRef*>(wsb + off.map1) : nullptr;
     Partial* parts = reinterpret_cast<Partial*>(wsb + off.parts);
-    Partial* parts1 = reinterpret_cast<Partial*>(wsb + off.parts1);
     if (!cached) {
         // tables first, tile maps next, header (with the signature) last
         WriteChunk c;
@@ -394,14 +391,14 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     const AdamScalars c = derive(hp);
     const float gscale = static_cast<float>(hp->grad_scale);
     const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
-    hipError_t e = launch_fused(first_mode, geom[0], hdr_dev, desc_dev, map0, tiles[0], sig, M, gscale, c, parts,
+    const FinalizeArgs fin{res_dev, reinterpret_cast<unsigned*>(wsb + kCounterOffset), external_sumsq,
+                           hp->max_grad_norm, skip};
+    hipError_t e = launch_fused(first_mode, geom[0], hdr_dev, desc_dev, map0, tiles[0], sig, M, gscale, c, parts, fin,
                                 nullptr, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
-    e = launch_finalize(parts, tiles[0], parts1, external_sumsq, hp->max_grad_norm, skip, res_dev, hdr_dev, sig, stream);
-    if (e != hipSuccess) return ZERO_ERR_HIP;
     if (two_pass) {
-        e = launch_fused(Mode::PassB, geom[1], hdr_dev, desc_dev, map1, tiles[1], sig, M, gscale, c, parts, res_dev,
-                         stream);
+        e = launch_fused(Mode::PassB, geom[1], hdr_dev, desc_dev, map1, tiles[1], sig, M, gscale, c, parts, fin,
+                         res_dev, stream);
         if (e != hipSuccess) return ZERO_ERR_HIP;
     }
     return ZERO_OK;

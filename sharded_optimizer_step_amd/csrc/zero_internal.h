@@ -95,9 +95,6 @@ struct alignas(16) Partial {
     uint32_t pad;
 };
 
-// Partials combined per workgroup by the first level of a two-level finalize.
-constexpr int kFinalizeChunk = 4096;
-
 struct alignas(16) PlanHeader {
     uint64_t signature;
     int64_t tiles[2];  // tiles of the fold pass (one partial each) and of the update pass
@@ -108,9 +105,22 @@ struct alignas(16) PlanHeader {
     int32_t pad;
 };
 
+// Byte offset, in the 256-byte header region of a zero_step workspace, of the
+// arrival counter of the fold pass (zero between launches).
+constexpr size_t kCounterOffset = 128;
+
+// What the last workgroup of a fold pass needs to write the result record.
+struct FinalizeArgs {
+    zero_result* res;
+    unsigned* counter;
+    double external;
+    double max_norm;
+    int skip;
+};
+
 // Byte offsets of the regions of a zero_step workspace.
 struct PlanOffsets {
-    size_t desc, ptrs, map0, map1, parts, parts1, gbuf, total;
+    size_t desc, ptrs, map0, map1, parts, gbuf, total;
 };
 
 // Payload of one plan-upload launch (carried in the kernel arguments).
@@ -140,17 +150,18 @@ hipError_t launch_reduce(const RankPtrs& ptrs, int Mc, bool first, bool last, fl
 hipError_t launch_check(const float* g, const Layout& L, Partial* parts, int grid, hipStream_t s);
 hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint16_t* out, const Layout& L,
                         const AdamScalars& c, const zero_result* res, int grid, hipStream_t s);
-// Norm/flag finalize over nparts partials into the result record; when
-// nparts > kFinalizeChunk and `level1` is given, a first launch combines
-// chunks of kFinalizeChunk partials into `level1`.
-hipError_t launch_finalize(const Partial* parts, int64_t nparts, Partial* level1, double external, double max_norm,
-                           int skip, zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s);
+// Norm/flag finalize of the composed entry points: nparts partials combined
+// in index order into the result record.
+hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external, double max_norm, int skip,
+                           zero_result* res, hipStream_t s);
 hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s);
 hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* map0, TileRef* map1, hipStream_t s);
-// One workgroup per tile: grid = tiles of the pass.
+// One workgroup per tile: grid = tiles of the pass. The fold passes (Full,
+// PassA) also finalize: their last workgroup writes the result record `fin`.
+// The update pass (PassB) reads coef and skip from `res`.
 hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map,
                         int64_t tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
-                        const zero_result* res, hipStream_t s);
+                        const FinalizeArgs& fin, const zero_result* res, hipStream_t s);
 
 // Workgroups of 256 threads that one kernel keeps resident on the current
 // device (occupancy x compute units), for the grid-stride launches.

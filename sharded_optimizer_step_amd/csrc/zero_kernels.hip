@@ -9,18 +9,22 @@
 //
 // This is streaming, HBM-bound work with no contraction, so there is no MFMA
 // here. Design points for CDNA4:
-//  - 256-thread workgroups (4 wave64); each thread owns 8 consecutive
-//    elements, so every replica read is one 16-byte load and a wave reads a
-//    contiguous 1 KiB per replica.
-//  - Tiles of 2048 elements are dealt to workgroups grid-stride
-//    (tile = blockIdx.x + k*gridDim.x) with the grid sized to the resident
-//    capacity: all workgroups sweep the buffers together, which keeps the
-//    pages in flight few (TLB reach with 64+ streams) and the load balanced.
+//  - Each thread owns runs of 8 consecutive elements, so every replica read
+//    is one 16-byte load and a wave reads a contiguous 1 KiB per replica.
+//  - The fused step launches one workgroup per tile (grid = tiles, in
+//    order), with a tile geometry per pass (threads x 8-element vectors per
+//    thread). Inside a tile the workgroup sweeps the replicas in lockstep, a
+//    barrier after each, so the reads in flight on the chip stay within a
+//    compact window of every replica (few open DRAM pages and TLB entries
+//    with 64+ streams).
 //  - The rank fold is a fixed ascending left fold in fp32; the sum of squares
 //    uses exact binary64 squares, a per-thread binary64 accumulator, a fixed
-//    wave butterfly and a fixed LDS order, then a one-workgroup finalize over
-//    per-workgroup partials in index order: bitwise repeatable, no atomics.
-//  - Replica reads and the once-written outputs use non-temporal accesses.
+//    wave butterfly and a fixed LDS order, and the per-workgroup partials are
+//    combined in index order by the last workgroup to finish: bitwise
+//    repeatable (atomics publish and count, they never add values).
+//  - The composed entry points (reduce, check, AdamW) use grid-stride sweeps
+//    of 2048-element tiles over a grid sized to the resident capacity.
+//  - Replica reads and the bf16 emit use non-temporal accesses.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -129,9 +133,10 @@ __device__ __forceinline__ void adam1(float g32, double coef, const AdamScalars&
 }
 
 // Per-workgroup reduction of (sum of squares, non-finite flag) in a fixed
-// order, written to one partial record.
+// order: a wave butterfly, then the waves in index order. The result is valid
+// in thread 0 only.
 template <int NT = kThreads>
-__device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial* __restrict__ out)
+__device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad)
 {
     __shared__ double s_acc[NT / 64];
     __shared__ uint32_t s_bad[NT / 64];
@@ -147,19 +152,80 @@ __device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial*
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        double a = s_acc[0];
-        uint32_t b = s_bad[0];
+        acc = s_acc[0];
+        bad = s_bad[0];
 #pragma unroll
         for (int w = 1; w < NT / 64; ++w) {
-            a += s_acc[w];
-            b |= s_bad[w];
+            acc += s_acc[w];
+            bad |= s_bad[w];
         }
+    }
+}
+
+// block_reduce, written to one partial record.
+template <int NT = kThreads>
+__device__ __forceinline__ void block_partial(double acc, uint32_t bad, Partial* __restrict__ out)
+{
+    block_reduce<NT>(acc, bad);
+    if (threadIdx.x == 0) {
         Partial p;
-        p.sumsq = a;
-        p.bad = b;
+        p.sumsq = acc;
+        p.bad = bad;
         p.pad = 0;
         *out = p;
     }
+}
+
+// ------------------------------------------------------------------ last-workgroup finalize
+//
+// A fold pass ends with its last-arriving workgroup turning the per-workgroup
+// partials into the result record, so a step needs no separate finalize
+// launch. Each workgroup publishes its partial with agent-scope atomic
+// exchanges and only then counts itself in with an agent-scope atomic add.
+// An atomic read-modify-write returns its old value once it has been
+// performed where the whole device sees it, and the add's operand is made to
+// depend on both returned values, so no workgroup is counted before its
+// partial is visible on every XCD. The workgroup that counts last reads the
+// partials with agent-scope atomic loads, which do not take a stale line
+// from its own XCD's L2. No release fence is used on purpose: on CDNA4 an
+// agent-scope release writes back the whole L2 of the XCD, and making every
+// workgroup wait for the write-back of the others' output lines cost 5-7% of
+// a two-pass step.
+
+// Zero, computed from x by an instruction the compiler cannot see through:
+// whatever consumes the result is issued only after x has arrived.
+__device__ __forceinline__ uint32_t zero_after(uint32_t x)
+{
+    uint32_t z;
+    asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(x));
+    return z;
+}
+
+// One thread: publish (sumsq, bad) as the partial at `slot`, then count the
+// workgroup in; returns the counter's value before the add.
+__device__ __forceinline__ unsigned publish_and_arrive(Partial* slot, double sumsq, uint32_t bad, unsigned* counter)
+{
+    const unsigned long long o1 = __hip_atomic_exchange(reinterpret_cast<unsigned long long*>(&slot->sumsq),
+                                                        static_cast<unsigned long long>(__double_as_longlong(sumsq)),
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t o2 = __hip_atomic_exchange(&slot->bad, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t dep = zero_after(static_cast<uint32_t>(o1) | static_cast<uint32_t>(o1 >> 32) | o2);
+    return __hip_atomic_fetch_add(counter, 1u + dep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The published partials 0..n-1 combined in a fixed order (thread i takes i,
+// i+NT, ...; then block_reduce); valid in thread 0.
+template <int NT>
+__device__ __forceinline__ void combine_published(Partial* parts, int64_t n, double& sumsq, uint32_t& bad)
+{
+    sumsq = 0.0;
+    bad = 0;
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+        sumsq += __longlong_as_double(static_cast<long long>(__hip_atomic_load(
+            reinterpret_cast<unsigned long long*>(&parts[i].sumsq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+        bad |= __hip_atomic_load(&parts[i].bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_reduce<NT>(sumsq, bad);
 }
 
 // ------------------------------------------------------------------ tile body
@@ -474,6 +540,55 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) do_tile<Op::Adam, 1, true>(x, k, c, t, acc, bad);
 }
 
+// The result record from the combined partials: norm, clip coefficient,
+// skip decision (clip rule: min(1, max/(norm + 1e-6)); NaN propagates).
+__device__ __forceinline__ zero_result make_record(double sumsq, uint32_t bad, double external, double max_norm,
+                                                   int skip)
+{
+    const double total = sumsq + external;
+    const double norm = sqrt(total);
+    double coef = 1.0;
+    if (max_norm > 0.0) {
+        coef = max_norm / (norm + 1e-6);
+        if (coef > 1.0) coef = 1.0;
+    }
+    zero_result r;
+    r.sumsq = total;
+    r.clip_coef = coef;
+    r.grad_norm = static_cast<float>(norm);
+    r.found_inf = bad != 0 ? 1 : 0;
+    r.skipped = (bad != 0 && skip != 0) ? 1 : 0;
+    r.status = ZERO_OK;
+    return r;
+}
+
+__device__ __forceinline__ zero_result stale_record()
+{
+    zero_result r;
+    r.sumsq = __builtin_nan("");
+    r.clip_coef = __builtin_nan("");
+    r.grad_norm = __builtin_nanf("");
+    r.found_inf = 0;
+    r.skipped = 1;
+    r.status = ZERO_ERR_STALE_WORKSPACE;
+    return r;
+}
+
+// Partials 0..n-1 written by an earlier launch, combined in the same fixed
+// order as combine_published; valid in thread 0.
+template <int NT>
+__device__ __forceinline__ void combine_partials(const Partial* __restrict__ parts, int64_t n, double& sumsq,
+                                                 uint32_t& bad)
+{
+    sumsq = 0.0;
+    bad = 0;
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+        sumsq += parts[i].sumsq;
+        bad |= parts[i].bad;
+    }
+    block_reduce<NT>(sumsq, bad);
+}
+
 // One workgroup per tile (grid = tiles): the workgroups in flight cover a
 // compact window of the buffers that advances as the dispatcher hands out
 // tiles in order, and the partial of tile t is written to parts[t] whatever
@@ -482,10 +597,15 @@ template <Mode MODE, int NT, int U>
 __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict__ hdr,
                                                    const TensorDesc* __restrict__ desc,
                                                    const TileRef* __restrict__ map, uint64_t sig, int M, float gscale,
-                                                   AdamScalars c, Partial* __restrict__ parts,
+                                                   AdamScalars c, Partial* __restrict__ parts, FinalizeArgs fin,
                                                    const zero_result* __restrict__ res)
 {
-    if (hdr->signature != sig) return;  // the workspace no longer holds this plan: write nothing
+    if (hdr->signature != sig) {  // the workspace no longer holds this plan: write nothing but the record
+        if constexpr (MODE != Mode::PassB) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) *fin.res = stale_record();
+        }
+        return;
+    }
     double coef = 1.0;
     if constexpr (MODE == Mode::PassB) {
         if (res->skipped != 0 || res->status != 0) return;
@@ -498,71 +618,35 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
     const TileRef tr = map[blockIdx.x];
     const Ctx x = ctx_of(desc[tr.tensor], M);
     big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
-    if constexpr (MODE != Mode::PassB) block_partial<NT>(acc, bad, parts + blockIdx.x);
-}
-
-// First level of a two-level finalize: workgroup w combines partials
-// [w*C, min(n, (w+1)*C)) in a fixed order.
-__global__ __launch_bounds__(kThreads) void partials_kernel(const Partial* __restrict__ parts, int64_t nparts,
-                                                            Partial* __restrict__ out)
-{
-    const int64_t b = static_cast<int64_t>(blockIdx.x) * kFinalizeChunk;
-    const int64_t e = b + kFinalizeChunk < nparts ? b + kFinalizeChunk : nparts;
-    double acc = 0.0;
-    uint32_t bad = 0;
-    for (int64_t i = b + threadIdx.x; i < e; i += kThreads) {
-        acc += parts[i].sumsq;
-        bad |= parts[i].bad;
+    if constexpr (MODE != Mode::PassB) {
+        // the last workgroup to arrive writes the record and re-arms the
+        // counter for the next launch
+        block_reduce<NT>(acc, bad);
+        __shared__ int s_last;
+        if (threadIdx.x == 0) s_last = publish_and_arrive(parts + blockIdx.x, acc, bad, fin.counter) == gridDim.x - 1;
+        __syncthreads();
+        if (s_last) {
+            double sumsq;
+            uint32_t nbad;
+            combine_published<NT>(parts, gridDim.x, sumsq, nbad);
+            if (threadIdx.x == 0) {
+                *fin.res = make_record(sumsq, nbad, fin.external, fin.max_norm, fin.skip);
+                __hip_atomic_store(fin.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
-    block_partial(acc, bad, out + blockIdx.x);
 }
 
 // One workgroup: combine the partials in index order, then the norm, the
 // clip coefficient and the skip decision.
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __restrict__ parts, int64_t nparts,
                                                             double external, double max_norm, int skip,
-                                                            zero_result* __restrict__ res,
-                                                            const PlanHeader* __restrict__ hdr, uint64_t sig)
+                                                            zero_result* __restrict__ res)
 {
-    if (hdr != nullptr && hdr->signature != sig) {
-        if (threadIdx.x == 0) {
-            zero_result r;
-            r.sumsq = __builtin_nan("");
-            r.grad_norm = __builtin_nanf("");
-            r.clip_coef = __builtin_nan("");
-            r.found_inf = 0;
-            r.skipped = 1;
-            r.status = ZERO_ERR_STALE_WORKSPACE;
-            *res = r;
-        }
-        return;
-    }
-    double acc = 0.0;
-    uint32_t bad = 0;
-    for (int64_t i = threadIdx.x; i < nparts; i += kThreads) {
-        acc += parts[i].sumsq;
-        bad |= parts[i].bad;
-    }
-    __shared__ Partial s_total;
-    block_partial(acc, bad, &s_total);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const double total = s_total.sumsq + external;
-        const double norm = sqrt(total);
-        double coef = 1.0;
-        if (max_norm > 0.0) {
-            coef = max_norm / (norm + 1e-6);
-            if (coef > 1.0) coef = 1.0;  // a NaN coefficient stays NaN
-        }
-        zero_result r;
-        r.sumsq = total;
-        r.grad_norm = static_cast<float>(norm);
-        r.clip_coef = coef;
-        r.found_inf = s_total.bad != 0 ? 1 : 0;
-        r.skipped = (s_total.bad != 0 && skip != 0) ? 1 : 0;
-        r.status = ZERO_OK;
-        *res = r;
-    }
+    double sumsq;
+    uint32_t bad;
+    combine_partials<kThreads>(parts, nparts, sumsq, bad);
+    if (threadIdx.x == 0) *res = make_record(sumsq, bad, external, max_norm, skip);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_write_kernel(uint8_t* __restrict__ ws, WriteChunk c)
@@ -651,14 +735,14 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
 template <Mode MODE>
 hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map, int64_t tiles,
                           uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
-                          const zero_result* res, hipStream_t s)
+                          const FinalizeArgs& fin, const zero_result* res, hipStream_t s)
 {
     if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const unsigned grid = static_cast<unsigned>(tiles);
     switch (geom) {
 #define ZERO_CASE(I, NTV, UV)                                                                          \
     case I:                                                                                            \
-        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, map, sig, M, gscale, c, parts, res); \
+        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, map, sig, M, gscale, c, parts, fin, res); \
         break;
         ZERO_FOR_EACH_GEOM(ZERO_CASE)
 #undef ZERO_CASE
@@ -691,18 +775,10 @@ hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint1
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const Partial* parts, int64_t nparts, Partial* level1, double external, double max_norm,
-                           int skip, zero_result* res, const PlanHeader* hdr, uint64_t sig, hipStream_t s)
+hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external, double max_norm, int skip,
+                           zero_result* res, hipStream_t s)
 {
-    if (nparts > kFinalizeChunk && level1 != nullptr) {
-        const int64_t g1 = (nparts + kFinalizeChunk - 1) / kFinalizeChunk;
-        partials_kernel<<<static_cast<unsigned>(g1), kThreads, 0, s>>>(parts, nparts, level1);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        parts = level1;
-        nparts = g1;
-    }
-    finalize_kernel<<<1, kThreads, 0, s>>>(parts, nparts, external, max_norm, skip, res, hdr, sig);
+    finalize_kernel<<<1, kThreads, 0, s>>>(parts, nparts, external, max_norm, skip, res);
     return hipGetLastError();
 }
 
@@ -721,12 +797,15 @@ hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* map0, TileR
 
 hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map,
                         int64_t tiles, uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
-                        const zero_result* res, hipStream_t s)
+                        const FinalizeArgs& fin, const zero_result* res, hipStream_t s)
 {
     switch (mode) {
-    case Mode::Full: return fused_dispatch<Mode::Full>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
-    case Mode::PassA: return fused_dispatch<Mode::PassA>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
-    case Mode::PassB: return fused_dispatch<Mode::PassB>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, res, s);
+    case Mode::Full:
+        return fused_dispatch<Mode::Full>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
+    case Mode::PassA:
+        return fused_dispatch<Mode::PassA>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
+    case Mode::PassB:
+        return fused_dispatch<Mode::PassB>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
     }
     return hipErrorInvalidValue;
 }

@@ -387,3 +387,28 @@ def test_empty_bucket_writes_the_record():
                 z.HParams(max_grad_norm=1.0), 4.0, None, res)
     r = z.read_result(res)
     assert r["sumsq"] == 4.0 and r["grad_norm"] == 2.0 and r["found_inf"] == 0
+
+
+@pytest.mark.parametrize("sizes,M,max_norm", [([300_001], 8, 0.0), ([4_000_000], 64, 0.0), ([100_003, 512], 4, 1e-3),
+                                               ([5_000_000], 8, 1.0)])
+def test_consecutive_steps_on_one_workspace_each_write_their_record(sizes, M, max_norm):
+    # The fold pass's last workgroup writes the record and re-arms its arrival
+    # counter; every step on the same workspace must report its own values.
+    case = Case(sizes, M, seed=96, grad_std=1e-3)
+    dts, hts = build(case)
+    hp = z.HParams(step=3, max_grad_norm=max_norm)
+    ws = z.workspace(z.zero_step_workspace_bytes(dts, M, hp))
+    res = z.new_result()
+    state = hts
+    for k, ext in enumerate([0.0, 0.5, 2.0, 0.125, 7.0]):
+        hp.step = 3 + k
+        z.zero_step(dts, hp, ext, ws, res)
+        r = z.read_result(res)
+        state, ro = oracle.zero_step(state, hp_oracle(hp), ext)
+        assert r["status"] == 0 and r["found_inf"] == 0
+        # 1e-9: the oracle's left-to-right fp64 sum of 4M squares is itself
+        # about 1e-11 from the exact sum; the steps differ by far more.
+        assert math.isclose(r["sumsq"], ro.sumsq, rel_tol=1e-9), (k, r, ro)
+        assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-9 * ro.clip_coef
+    for d, h in zip(dts, state):
+        assert_tensor_matches(d, h, "after 5 steps")
