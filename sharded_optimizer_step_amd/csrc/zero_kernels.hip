@@ -43,15 +43,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ helpers
 
+// Every buffer of the step is device (global) memory, so the 16-byte accesses
+// go through the global address space: global_* instructions with a scalar
+// base, rather than flat accesses that also count against the LDS counter.
+#define ZERO_GLOBAL __attribute__((address_space(1)))
+#define ZERO_CONSTANT __attribute__((address_space(4)))
+
 __device__ __forceinline__ u32x4 ld_nt(const uint16_t* p)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return __builtin_nontemporal_load((const ZERO_GLOBAL u32x4*)p);
 }
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-__device__ __forceinline__ void st_nt(uint16_t* p, u32x4 v)
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const ZERO_GLOBAL f32x4*)p; }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *(ZERO_GLOBAL f32x4*)p = v; }
+__device__ __forceinline__ void st_nt(uint16_t* p, u32x4 v) { __builtin_nontemporal_store(v, (ZERO_GLOBAL u32x4*)p); }
+
+// Base address of replica r from a plan's rank-pointer table in the
+// workspace. The table is written before the launch and not modified during
+// it, so it is read through the constant address space: a scalar load served
+// by the scalar cache instead of a vector round trip in front of every
+// replica sweep.
+__device__ __forceinline__ const uint16_t* rank_ptr(const uint16_t* const* gp, int r)
 {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    return reinterpret_cast<const uint16_t*>(((const ZERO_CONSTANT uint64_t*)gp)[r]);
 }
 
 // bf16 -> fp32 is exact: the code is the upper half of the binary32 encoding.
@@ -397,7 +410,7 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
     if constexpr (OP == Op::Full || OP == Op::PassA) {
         bool ok[U];
         float s[U][8];
-        const uint16_t* p0 = x.gp[0] + x.head;
+        const uint16_t* p0 = rank_ptr(x.gp, 0) + x.head;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             ok[u] = v0 + u * 64 < x.nvec;
@@ -411,7 +424,7 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
         __syncthreads();
 #pragma unroll 1
         for (int r = 1; r < x.M; ++r) {
-            const uint16_t* p = x.gp[r] + x.head;
+            const uint16_t* p = rank_ptr(x.gp, r) + x.head;
             u32x4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ok[u] ? ld_nt(p + (v0 + u * 64) * kVec) : u32x4{0u, 0u, 0u, 0u};
