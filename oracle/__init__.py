@@ -52,6 +52,16 @@ class _Tensor(ctypes.Structure):
                 ("param_out", ctypes.c_void_p)]
 
 
+class _LossScale(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("inv_scale", ctypes.c_float), ("good_steps", ctypes.c_int32),
+                ("overflows", ctypes.c_int32)]
+
+
+class _LossScaleConfig(ctypes.Structure):
+    _fields_ = [("initial_scale_power", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("hysteresis", ctypes.c_int32), ("min_scale", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -70,6 +80,10 @@ def lib():
         L.oracle_zero_step.argtypes = [ctypes.POINTER(_Tensor), i32, i32, ctypes.POINTER(_Hparams), dbl,
                                        ctypes.POINTER(_Result)]
         L.oracle_zero_step.restype = i32
+        L.oracle_loss_scale_init.argtypes = [ctypes.POINTER(_LossScaleConfig), ctypes.POINTER(_LossScale)]
+        L.oracle_loss_scale_update.argtypes = [ctypes.POINTER(_LossScaleConfig), i32, ctypes.POINTER(_LossScale)]
+        L.oracle_loss_scale_init.restype = None
+        L.oracle_loss_scale_update.restype = None
         for f in ("oracle_bf16_to_f32", "oracle_f32_to_bf16", "oracle_reduce", "oracle_check",
                   "oracle_finalize", "oracle_adamw"):
             getattr(L, f).restype = None
@@ -207,6 +221,61 @@ def zero_step(tensors: Sequence[TensorState], hp: HParams, external_sumsq: float
     if rc != 0:
         raise MemoryError("oracle_zero_step: out of host memory")
     return new, Result(r.sumsq, r.grad_norm, r.clip_coef, r.found_inf, r.skipped)
+
+
+# --------------------------------------------------------------------------
+# Dynamic loss scale (see oracle_loss_scale_update in zero_oracle.c for the
+# rule and the passages it reads).
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LossScaleConfig:
+    initial_scale_power: int = 12
+    window: int = 1000
+    hysteresis: int = 2
+    min_scale: float = 1.0
+
+    def _c(self) -> _LossScaleConfig:
+        return _LossScaleConfig(self.initial_scale_power, self.window, self.hysteresis, self.min_scale)
+
+
+@dataclasses.dataclass(frozen=True)
+class LossScale:
+    scale: float
+    inv_scale: float
+    good_steps: int = 0
+    overflows: int = 0
+
+    def _c(self) -> _LossScale:
+        return _LossScale(self.scale, self.inv_scale, self.good_steps, self.overflows)
+
+
+def _ls(c: _LossScale) -> LossScale:
+    return LossScale(c.scale, c.inv_scale, c.good_steps, c.overflows)
+
+
+def loss_scale_init(cfg: LossScaleConfig) -> LossScale:
+    c = _LossScale()
+    lib().oracle_loss_scale_init(ctypes.byref(cfg._c()), ctypes.byref(c))
+    return _ls(c)
+
+
+def loss_scale_update(state: LossScale, cfg: LossScaleConfig, found_inf: int) -> LossScale:
+    c = state._c()
+    lib().oracle_loss_scale_update(ctypes.byref(cfg._c()), int(bool(found_inf)), ctypes.byref(c))
+    return _ls(c)
+
+
+def zero_step_amp(tensors: Sequence[TensorState], hp: HParams, cfg: LossScaleConfig, state: LossScale,
+                  external_sumsq: float = 0.0):
+    """One AMP step with a dynamic loss scale: the fp32 sum is multiplied by
+    grad_scale x inv_scale (a binary32 product), a step with a non-finite
+    gradient is skipped, then the scale moves on the step's flag.
+    Returns (new TensorStates, Result, new LossScale)."""
+    mult = float(np.float32(hp.grad_scale) * np.float32(state.inv_scale))
+    h = dataclasses.replace(hp, grad_scale=mult, skip_on_nonfinite=1)
+    new, res = zero_step(tensors, h, external_sumsq)
+    return new, res, loss_scale_update(state, cfg, res.found_inf)
 
 
 # --------------------------------------------------------------------------

@@ -50,6 +50,11 @@
  *                master value (the shard the all-gather would broadcast;
  *                [CS336 L7] Stage 1 step 4).
  *
+ *   7. scale     (AMP with a dynamic loss scale) after the step, the loss
+ *                scale S moves on the step's non-finite flag: see
+ *                oracle_loss_scale_update below ([5D post] 4.2 fp16 block,
+ *                3.2 trap 3).
+ *
  * Compile with -O2 -ffp-contract=off and without -ffast-math: the binary32
  * fold of step 1 must be exactly the sequence of rounded adds written here.
  */
@@ -274,4 +279,73 @@ done:
     for (int32_t t = 0; t < T; ++t) free(gs[t]);
     free(gs);
     return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 7: the dynamic loss scale.                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * [5D post] 4.2 configures the fp16 loss scale with loss_scale 0 (dynamic),
+ * initial_scale_power, loss_scale_window, hysteresis and min_loss_scale, and
+ * 3.2 trap 3 describes the scaler's cycle (scale the loss, step on unscaled
+ * gradients, update the scale). The pages print the knobs, not the rule; the
+ * reading taken from their names:
+ *   - S starts at 2^initial_scale_power.
+ *   - A step whose unscaled gradient holds a non-finite value is an overflow
+ *     (the step itself is skipped). The hysteresis-th overflow in a row,
+ *     counted since the last clean step or the last halving, halves S, never
+ *     below min_loss_scale, and restarts the count.
+ *   - A clean step clears the overflow count. The loss_scale_window-th clean
+ *     step in a row, counted since the last overflow or the last doubling,
+ *     doubles S, unless 2S is not a finite binary32 value, and restarts the
+ *     count.
+ *   - S is a binary32 value; the step multiplies the fp32 sum by
+ *     inv_scale = 1/S rounded to binary32 (exact while S is a power of two).
+ * With hysteresis 1 this is the growth/backoff rule of a gradient scaler
+ * with growth factor 2, backoff factor 1/2 and growth interval
+ * loss_scale_window.
+ */
+
+typedef struct {
+    float scale;        /* S */
+    float inv_scale;    /* 1/S, rounded to binary32 */
+    int32_t good_steps; /* clean steps in a row since the last overflow or doubling */
+    int32_t overflows;  /* overflows in a row since the last clean step or halving */
+} oracle_loss_scale;
+
+typedef struct {
+    int32_t initial_scale_power;
+    int32_t window;     /* loss_scale_window, >= 1 */
+    int32_t hysteresis; /* >= 1 */
+    float min_scale;    /* min_loss_scale, > 0 */
+} oracle_loss_scale_config;
+
+void oracle_loss_scale_init(const oracle_loss_scale_config* c, oracle_loss_scale* s)
+{
+    s->scale = (float)ldexp(1.0, c->initial_scale_power);
+    s->inv_scale = 1.0f / s->scale;
+    s->good_steps = 0;
+    s->overflows = 0;
+}
+
+void oracle_loss_scale_update(const oracle_loss_scale_config* c, int32_t found_inf, oracle_loss_scale* s)
+{
+    if (found_inf) {
+        s->good_steps = 0;
+        s->overflows += 1;
+        if (s->overflows >= c->hysteresis) {
+            const float half = s->scale / 2.0f;
+            s->scale = half < c->min_scale ? c->min_scale : half;
+            s->overflows = 0;
+        }
+    } else {
+        s->overflows = 0;
+        s->good_steps += 1;
+        if (s->good_steps >= c->window) {
+            const float twice = s->scale * 2.0f;
+            if (isfinite(twice)) s->scale = twice;
+            s->good_steps = 0;
+        }
+    }
+    s->inv_scale = 1.0f / s->scale;
 }
