@@ -177,6 +177,80 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
 int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
               double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Dynamic loss scale (AMP).
+ *
+ * gsyq.cn/news/457874 configures the fp16 loss scale with the fp16 block of
+ * its section 4.2 listing (loss_scale 0 = dynamic, initial_scale_power,
+ * loss_scale_window, hysteresis, min_loss_scale) and describes the scaler's
+ * cycle in section 3.2 trap 3 (scale the loss, step on unscaled gradients,
+ * update the scale). The pages name the knobs, not the rule; the rule read
+ * from them:
+ *   - S starts at 2^initial_scale_power;
+ *   - a step whose unscaled reduced gradient holds inf/NaN is skipped and is
+ *     an overflow; the hysteresis-th overflow in a row (counted since the last
+ *     clean step or halving) halves S, never below min_scale, and restarts the
+ *     count;
+ *   - a clean step clears the overflow count; the window-th clean step in a
+ *     row (counted since the last overflow or doubling) doubles S unless 2S is
+ *     not a finite binary32 value, and restarts the count;
+ *   - inv_scale = 1/S rounded to binary32 (exact while S is a power of two).
+ * The state stays in device memory: a training loop moves it without a host
+ * synchronisation.
+ * ------------------------------------------------------------------------ */
+
+/* Loss-scale state, 16 bytes, device memory, written by the library. */
+typedef struct zero_loss_scale {
+    float scale;        /* S: the factor the loss was multiplied by */
+    float inv_scale;    /* 1/S rounded to binary32 */
+    int32_t good_steps; /* clean steps in a row since the last overflow or doubling */
+    int32_t overflows;  /* overflowing steps in a row since the last clean step or halving */
+} zero_loss_scale;
+
+/* Loss-scale knobs (host memory, read during the call). */
+typedef struct zero_loss_scale_config {
+    int32_t initial_scale_power; /* S starts at 2^power; -126 <= power <= 127 */
+    int32_t window;              /* loss_scale_window: clean steps per doubling, >= 1 */
+    int32_t hysteresis;          /* overflows in a row per halving, >= 1 */
+    float min_scale;             /* min_loss_scale: finite, > 0 */
+} zero_loss_scale_config;
+
+/*
+ * zero_loss_scale_init -- write the initial state (S = 2^initial_scale_power,
+ * counts 0) to ls_dev (device, 16 bytes).
+ */
+int zero_loss_scale_init(const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, hipStream_t stream);
+
+/*
+ * zero_loss_scale_update -- move the state ls_dev on the found_inf flag of
+ * the result record res_dev (device) of a step that used it, e.g. after
+ * zero_shard_reduce with grad_scale = inv_scale and zero_grad_check_norm.
+ * A record whose status is not ZERO_OK leaves the state unchanged.
+ */
+int zero_loss_scale_update(const zero_loss_scale_config* cfg, const zero_result* res_dev, zero_loss_scale* ls_dev,
+                           hipStream_t stream);
+
+/*
+ * zero_step_amp_workspace_bytes -- workspace size for zero_step_amp (always
+ * the two-pass plan). Returns 0 on invalid arguments.
+ */
+size_t zero_step_amp_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp);
+
+/*
+ * zero_step_amp -- zero_step with the dynamic loss scale in ls_dev: the fp32
+ * sum is multiplied by fl32(grad_scale) * inv_scale (a binary32 product read
+ * from ls_dev by the device, so the host never needs S); a step with any
+ * inf/NaN in the unscaled gradient is always skipped (skip_on_nonfinite is
+ * ignored); after the fold, the state moves on the step's found_inf. No
+ * extra launch: the workgroup that writes the result record also updates
+ * ls_dev. ls_dev must not change while the call runs, and two calls that share
+ * ls_dev must be ordered (one stream). Other arguments and errors as for
+ * zero_step; the workspace size is zero_step_amp_workspace_bytes(...).
+ */
+int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                  const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, double external_sumsq, void* ws,
+                  size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
+
 /*
  * zero_workspace_forget -- drop the host-side record that `ws` holds the
  * tensor table of an earlier zero_step call. Call it before freeing or

@@ -39,7 +39,9 @@ RESULT_BYTES = 32
 
 # Every symbol the C ABI exports (include/zero_step.h).
 EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_grad_check_norm", "zero_adamw_step",
-           "zero_step_workspace_bytes", "zero_step", "zero_workspace_forget", "zero_status_string")
+           "zero_step_workspace_bytes", "zero_step", "zero_loss_scale_init", "zero_loss_scale_update",
+           "zero_step_amp_workspace_bytes", "zero_step_amp", "zero_workspace_forget", "zero_status_string")
+LOSS_SCALE_BYTES = 16
 
 
 class _CHparams(ctypes.Structure):
@@ -52,6 +54,11 @@ class _CHparams(ctypes.Structure):
 class _CTensor(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class _CLossScaleConfig(ctypes.Structure):
+    _fields_ = [("initial_scale_power", ctypes.c_int32), ("window", ctypes.c_int32), ("hysteresis", ctypes.c_int32),
+                ("min_scale", ctypes.c_float)]
 
 
 class ZeroError(RuntimeError):
@@ -84,6 +91,15 @@ def lib() -> ctypes.CDLL:
         L.zero_step_workspace_bytes.restype = sz
         L.zero_step.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams), dbl, vp, sz, vp, vp]
         L.zero_step.restype = ctypes.c_int
+        L.zero_loss_scale_init.argtypes = [ctypes.POINTER(_CLossScaleConfig), vp, vp]
+        L.zero_loss_scale_init.restype = ctypes.c_int
+        L.zero_loss_scale_update.argtypes = [ctypes.POINTER(_CLossScaleConfig), vp, vp, vp]
+        L.zero_loss_scale_update.restype = ctypes.c_int
+        L.zero_step_amp_workspace_bytes.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams)]
+        L.zero_step_amp_workspace_bytes.restype = sz
+        L.zero_step_amp.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams),
+                                    ctypes.POINTER(_CLossScaleConfig), vp, dbl, vp, sz, vp, vp]
+        L.zero_step_amp.restype = ctypes.c_int
         L.zero_workspace_forget.argtypes = [vp]
         L.zero_workspace_forget.restype = ctypes.c_int
         L.zero_status_string.argtypes = [ctypes.c_int]
@@ -241,6 +257,64 @@ def zero_step(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float,
     wsb = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().zero_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), _ptr(ws), wsb,
                            res.data_ptr(), _stream(stream)), "zero_step")
+
+
+@dataclasses.dataclass
+class LossScaleConfig:
+    """Dynamic loss-scale knobs (names of the fp16 block of a
+    deepspeed_config.json; defaults are the values printed there)."""
+    initial_scale_power: int = 12
+    window: int = 1000
+    hysteresis: int = 2
+    min_scale: float = 1.0
+
+    def _c(self) -> _CLossScaleConfig:
+        return _CLossScaleConfig(int(self.initial_scale_power), int(self.window), int(self.hysteresis),
+                                 float(self.min_scale))
+
+
+def new_loss_scale(device=None) -> torch.Tensor:
+    """A 16-byte device buffer for the zero_loss_scale state."""
+    return torch.zeros(LOSS_SCALE_BYTES, dtype=torch.uint8, device=device or "cuda")
+
+
+def read_loss_scale(ls: torch.Tensor) -> dict:
+    """Copy the state to the host (synchronizes with its stream)."""
+    scale, inv_scale, good_steps, overflows = struct.unpack("<ffii", bytes(ls.cpu().numpy().tobytes()))
+    return dict(scale=scale, inv_scale=inv_scale, good_steps=good_steps, overflows=overflows)
+
+
+def zero_loss_scale_init(cfg: LossScaleConfig, ls: torch.Tensor, stream=None) -> None:
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    c = cfg._c()
+    _check(lib().zero_loss_scale_init(ctypes.byref(c), ls.data_ptr(), _stream(stream)), "zero_loss_scale_init")
+
+
+def zero_loss_scale_update(cfg: LossScaleConfig, res: torch.Tensor, ls: torch.Tensor, stream=None) -> None:
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    c = cfg._c()
+    _check(lib().zero_loss_scale_update(ctypes.byref(c), res.data_ptr(), ls.data_ptr(), _stream(stream)),
+           "zero_loss_scale_update")
+
+
+def zero_step_amp_workspace_bytes(tensors: Sequence[ZeroTensor], M: int, hp: HParams) -> int:
+    arr, keep, _ = _ctensors(tensors, check=False)
+    h = hp._c()
+    return int(lib().zero_step_amp_workspace_bytes(arr, len(tensors), int(M), ctypes.byref(h)))
+
+
+def zero_step_amp(tensors: Sequence[ZeroTensor], hp: HParams, cfg: LossScaleConfig, ls: torch.Tensor,
+                  external_sumsq: float, ws: Optional[torch.Tensor], res: torch.Tensor, stream=None) -> None:
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    arr, keep, M = _ctensors(tensors, check=True)
+    h = hp._c()
+    c = cfg._c()
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_step_amp(arr, len(tensors), M, ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
+                               float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
+           "zero_step_amp")
 
 
 def zero_workspace_forget(ws: torch.Tensor) -> None:

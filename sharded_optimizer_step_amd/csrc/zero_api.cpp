@@ -54,6 +54,12 @@ AdamScalars derive(const zero_adamw_hparams* hp)
     return c;
 }
 
+bool loss_scale_config_ok(const zero_loss_scale_config* c)
+{
+    return c != nullptr && c->initial_scale_power >= -126 && c->initial_scale_power <= 127 && c->window >= 1 &&
+           c->hysteresis >= 1 && std::isfinite(c->min_scale) && c->min_scale > 0.0f;
+}
+
 bool two_pass_of(const zero_adamw_hparams* hp) { return hp->max_grad_norm > 0.0 || hp->skip_on_nonfinite != 0; }
 
 // Vector mode needs one head length h in [0, 8) at which every bf16 pointer
@@ -256,8 +262,12 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
     return plan_offsets(tensors, T, M, two_pass_of(hp)).total;
 }
 
-int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
-              void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
+// The fused step; `ls` (with its config `lscfg`) non-null for the AMP form:
+// always two-pass, always skipping on a non-finite gradient, the multiplier
+// read from the device state, which the fold's last workgroup then moves.
+static int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
+                     void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream,
+                     const zero_loss_scale_config* lscfg, zero_loss_scale* ls)
 {
     // ---- arguments
     if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr)
@@ -273,11 +283,14 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
             if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
         total_n += x.n;
     }
-    const bool two_pass = two_pass_of(hp);
-    const int skip = hp->skip_on_nonfinite != 0;
-    if (total_n == 0)
-        return hip_status(
-            launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, stream));
+    const bool amp = ls != nullptr;
+    const bool two_pass = amp || two_pass_of(hp);
+    const int skip = amp || hp->skip_on_nonfinite != 0;
+    if (total_n == 0) {
+        hipError_t e = launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, stream);
+        if (e == hipSuccess && amp) e = launch_loss_scale_update(*lscfg, res_dev, ls, stream);
+        return hip_status(e);
+    }
     if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
     const PlanOffsets off = plan_offsets(tensors, T, M, two_pass);
     if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
@@ -391,8 +404,9 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     const AdamScalars c = derive(hp);
     const float gscale = static_cast<float>(hp->grad_scale);
     const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
-    const FinalizeArgs fin{res_dev, reinterpret_cast<unsigned*>(wsb + kCounterOffset), external_sumsq,
-                           hp->max_grad_norm, skip};
+    FinalizeArgs fin{res_dev, reinterpret_cast<unsigned*>(wsb + kCounterOffset), external_sumsq,
+                     hp->max_grad_norm, skip, ls, {}};
+    if (amp) fin.lscfg = *lscfg;
     hipError_t e = launch_fused(first_mode, geom[0], hdr_dev, desc_dev, map0, tiles[0], sig, M, gscale, c, parts, fin,
                                 nullptr, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
@@ -402,6 +416,47 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
         if (e != hipSuccess) return ZERO_ERR_HIP;
     }
     return ZERO_OK;
+}
+
+int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
+              void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
+{
+    return step_impl(tensors, T, M, hp, external_sumsq, ws, ws_bytes, res_dev, stream, nullptr, nullptr);
+}
+
+int zero_loss_scale_init(const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, hipStream_t stream)
+{
+    if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    zero_loss_scale s;
+    s.scale = static_cast<float>(std::ldexp(1.0, cfg->initial_scale_power));
+    s.inv_scale = static_cast<float>(1.0 / static_cast<double>(s.scale));
+    s.good_steps = 0;
+    s.overflows = 0;
+    return hip_status(launch_loss_scale_init(s, ls_dev, stream));
+}
+
+int zero_loss_scale_update(const zero_loss_scale_config* cfg, const zero_result* res_dev, zero_loss_scale* ls_dev,
+                           hipStream_t stream)
+{
+    if (!loss_scale_config_ok(cfg) || res_dev == nullptr || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_loss_scale_update(*cfg, res_dev, ls_dev, stream));
+}
+
+size_t zero_step_amp_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp)) return 0;
+    if (T > 0 && tensors == nullptr) return 0;
+    for (int32_t t = 0; t < T; ++t)
+        if (tensors[t].n < 0) return 0;
+    return plan_offsets(tensors, T, M, true).total;
+}
+
+int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                  const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, double external_sumsq, void* ws,
+                  size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
+{
+    if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    return step_impl(tensors, T, M, hp, external_sumsq, ws, ws_bytes, res_dev, stream, cfg, ls_dev);
 }
 
 int zero_workspace_forget(const void* ws)

@@ -109,13 +109,16 @@ struct alignas(16) PlanHeader {
 // arrival counter of the fold pass (zero between launches).
 constexpr size_t kCounterOffset = 128;
 
-// What the last workgroup of a fold pass needs to write the result record.
+// What the last workgroup of a fold pass needs to write the result record
+// and, in the AMP form (ls non-null), to move the loss scale.
 struct FinalizeArgs {
     zero_result* res;
     unsigned* counter;
     double external;
     double max_norm;
     int skip;
+    zero_loss_scale* ls;           // null unless AMP; the fold also reads its inv_scale
+    zero_loss_scale_config lscfg;  // meaningful when ls is non-null
 };
 
 // Byte offsets of the regions of a zero_step workspace.
@@ -154,6 +157,9 @@ hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint1
 // in index order into the result record.
 hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external, double max_norm, int skip,
                            zero_result* res, hipStream_t s);
+hipError_t launch_loss_scale_init(const zero_loss_scale& s, zero_loss_scale* ls, hipStream_t st);
+hipError_t launch_loss_scale_update(const zero_loss_scale_config& c, const zero_result* res, zero_loss_scale* ls,
+                                    hipStream_t st);
 hipError_t launch_plan_write(uint8_t* ws, const WriteChunk& c, hipStream_t s);
 hipError_t launch_plan_tiles(const TensorDesc* desc, int T, TileRef* map0, TileRef* map1, hipStream_t s);
 // One workgroup per tile: grid = tiles of the pass. The fold passes (Full,

@@ -587,6 +587,36 @@ __device__ __forceinline__ zero_result stale_record()
     return r;
 }
 
+// One move of the dynamic loss scale on a step's overflow flag (the rule is
+// stated with zero_loss_scale in zero_step.h: hysteresis-th overflow in a row
+// halves S down to min_scale, window-th clean step in a row doubles it while
+// 2S is finite). 1/S is formed in binary64 and rounded once, which equals the
+// correctly rounded binary32 quotient (53 >= 2*24 + 2).
+__device__ __forceinline__ void loss_scale_move(const zero_loss_scale_config& c, bool overflow,
+                                                zero_loss_scale* __restrict__ p)
+{
+    zero_loss_scale s = *p;
+    if (overflow) {
+        s.good_steps = 0;
+        s.overflows += 1;
+        if (s.overflows >= c.hysteresis) {
+            const float half = s.scale / 2.0f;
+            s.scale = half < c.min_scale ? c.min_scale : half;
+            s.overflows = 0;
+        }
+    } else {
+        s.overflows = 0;
+        s.good_steps += 1;
+        if (s.good_steps >= c.window) {
+            const float twice = s.scale * 2.0f;
+            if (__builtin_isfinite(twice)) s.scale = twice;
+            s.good_steps = 0;
+        }
+    }
+    s.inv_scale = static_cast<float>(1.0 / static_cast<double>(s.scale));
+    *p = s;
+}
+
 // Partials 0..n-1 written by an earlier launch, combined in the same fixed
 // order as combine_published; valid in thread 0.
 template <int NT>
@@ -624,6 +654,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
         if (res->skipped != 0 || res->status != 0) return;
         coef = res->clip_coef;
     }
+    if constexpr (MODE != Mode::PassB) {
+        if (fin.ls != nullptr) gscale = gscale * fin.ls->inv_scale;  // AMP: the scale of this step
+    }
     constexpr Op OP = MODE == Mode::Full ? Op::Full : (MODE == Mode::PassA ? Op::PassA : Op::Adam);
     const Scal k{gscale, coef, false};
     double acc = 0.0;
@@ -644,6 +677,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
             combine_published<NT>(parts, gridDim.x, sumsq, nbad);
             if (threadIdx.x == 0) {
                 *fin.res = make_record(sumsq, nbad, fin.external, fin.max_norm, fin.skip);
+                // every other workgroup has arrived, so none still reads inv_scale
+                if (fin.ls != nullptr) loss_scale_move(fin.lscfg, nbad != 0, fin.ls);
                 __hip_atomic_store(fin.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -660,6 +695,17 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
     uint32_t bad;
     combine_partials<kThreads>(parts, nparts, sumsq, bad);
     if (threadIdx.x == 0) *res = make_record(sumsq, bad, external, max_norm, skip);
+}
+
+__global__ void loss_scale_init_kernel(zero_loss_scale s, zero_loss_scale* __restrict__ ls)
+{
+    if (threadIdx.x == 0) *ls = s;
+}
+
+__global__ void loss_scale_update_kernel(zero_loss_scale_config c, const zero_result* __restrict__ res,
+                                         zero_loss_scale* __restrict__ ls)
+{
+    if (threadIdx.x == 0 && res->status == ZERO_OK) loss_scale_move(c, res->found_inf != 0, ls);
 }
 
 __global__ __launch_bounds__(kThreads) void plan_write_kernel(uint8_t* __restrict__ ws, WriteChunk c)
@@ -792,6 +838,19 @@ hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external
                            zero_result* res, hipStream_t s)
 {
     finalize_kernel<<<1, kThreads, 0, s>>>(parts, nparts, external, max_norm, skip, res);
+    return hipGetLastError();
+}
+
+hipError_t launch_loss_scale_init(const zero_loss_scale& s, zero_loss_scale* ls, hipStream_t st)
+{
+    loss_scale_init_kernel<<<1, 64, 0, st>>>(s, ls);
+    return hipGetLastError();
+}
+
+hipError_t launch_loss_scale_update(const zero_loss_scale_config& c, const zero_result* res, zero_loss_scale* ls,
+                                    hipStream_t st)
+{
+    loss_scale_update_kernel<<<1, 64, 0, st>>>(c, res, ls);
     return hipGetLastError();
 }
 

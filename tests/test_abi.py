@@ -47,13 +47,17 @@ def test_struct_layouts_match_header(tmp_path):
     """Compile the header with gcc and compare every field offset with the
     ctypes mirrors of the Python binding."""
     import subprocess
-    fields = {"zero_adamw_hparams": z._CHparams, "zero_tensor": z._CTensor}
+    fields = {"zero_adamw_hparams": z._CHparams, "zero_tensor": z._CTensor,
+              "zero_loss_scale_config": z._CLossScaleConfig}
     body = []
     for cname, cls in fields.items():
         body.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in cls._fields_:
             body.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
     body.append('printf("zero_result %zu\\n", sizeof(zero_result));')
+    body.append('printf("zero_loss_scale %zu\\n", sizeof(zero_loss_scale));')
+    for f in ("scale", "inv_scale", "good_steps", "overflows"):
+        body.append(f'printf("zero_loss_scale.{f} %zu\\n", offsetof(zero_loss_scale, {f}));')
     src = tmp_path / "layout.c"
     src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"zero_step.h\"\nint main(void){" +
                    "".join(body) + "return 0;}\n")
@@ -67,6 +71,9 @@ def test_struct_layouts_match_header(tmp_path):
         for f, _ in cls._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
     assert int(got["zero_result"]) == z.RESULT_BYTES
+    # read_loss_scale unpacks "<ffii"
+    assert int(got["zero_loss_scale"]) == z.LOSS_SCALE_BYTES
+    assert [int(got[f"zero_loss_scale.{f}"]) for f in ("scale", "inv_scale", "good_steps", "overflows")] == [0, 4, 8, 12]
 
 
 def test_status_strings():
@@ -168,3 +175,42 @@ def test_forget_needs_a_pointer():
     L = z.lib()
     assert L.zero_workspace_forget(None) == 1
     assert L.zero_workspace_forget(ctypes.c_void_p(4096)) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(initial_scale_power=128), dict(initial_scale_power=-127), dict(window=0),
+                                dict(hysteresis=0), dict(min_scale=0.0), dict(min_scale=-1.0),
+                                dict(min_scale=float("inf")), dict(min_scale=float("nan"))])
+def test_bad_loss_scale_config_is_rejected_without_launch(kw):
+    L = z.lib()
+    c = z.LossScaleConfig(**kw)._c()
+    ls, res = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert L.zero_loss_scale_init(ctypes.byref(c), ls, None) == 1
+    assert L.zero_loss_scale_update(ctypes.byref(c), res, ls, None) == 1
+    h = _hp()
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(100, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_amp_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), ctypes.byref(c), ls, 0.0, 1 << 24, need, res, None) == 1
+
+
+def test_loss_scale_entry_points_need_their_buffers():
+    L = z.lib()
+    c = z.LossScaleConfig()._c()
+    assert L.zero_loss_scale_init(None, ctypes.c_void_p(1 << 20), None) == 1
+    assert L.zero_loss_scale_init(ctypes.byref(c), None, None) == 1
+    assert L.zero_loss_scale_update(ctypes.byref(c), None, ctypes.c_void_p(1 << 20), None) == 1
+    assert L.zero_loss_scale_update(ctypes.byref(c), ctypes.c_void_p(1 << 21), None, None) == 1
+    h = _hp()  # no clipping, no skip: zero_step alone would be single-pass
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(100, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_amp_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    assert need == L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(_hp(skip_on_nonfinite=1)))
+    assert need > L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    res = ctypes.c_void_p(1 << 21)
+    assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), ctypes.byref(c), None, 0.0, 1 << 24, need, res, None) == 1
+    assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), None, ctypes.c_void_p(1 << 20), 0.0, 1 << 24, need, res,
+                           None) == 1
+    assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), ctypes.byref(c), ctypes.c_void_p(1 << 20), 0.0, 1 << 24,
+                           need - 1, res, None) == 2
