@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 4 GiB device copy (HBM counter calibration)")
     p.add_argument("--stagger", type=int, default=0, help="bytes added between consecutive replica bases")
+    p.add_argument("--amp", action="store_true",
+                   help="step with zero_step_amp: the loss scale held on the device, starting at the workload's "
+                        "1/grad_scale (a power of two), window 1000, hysteresis 2")
     return p.parse_args()
 
 
@@ -145,13 +148,28 @@ def main():
     tensors = build_workload(w, a.stagger)
     hp0 = w.hparams()
     hp = z.HParams(**hp0)
-    ws = z.workspace(z.zero_step_workspace_bytes(tensors, w.M, hp))
     res = z.new_result()
     stream = torch.cuda.current_stream()
+    if a.amp:
+        import math
+        power = -math.log2(hp.grad_scale)
+        if power != int(power):
+            sys.exit(f"bench.py --amp: workload grad_scale {hp.grad_scale} is not a power of two")
+        lscfg = z.LossScaleConfig(initial_scale_power=int(power), window=1000, hysteresis=2, min_scale=1.0)
+        hp.grad_scale = 1.0  # the multiplier now comes from the device state
+        ls = z.new_loss_scale()
+        z.zero_loss_scale_init(lscfg, ls, stream)
+        ws = z.workspace(z.zero_step_amp_workspace_bytes(tensors, w.M, hp))
 
-    def step(i):
-        hp.step = hp0["step"] + i
-        z.zero_step(tensors, hp, 0.0, ws, res, stream)
+        def step(i):
+            hp.step = hp0["step"] + i
+            z.zero_step_amp(tensors, hp, lscfg, ls, 0.0, ws, res, stream)
+    else:
+        ws = z.workspace(z.zero_step_workspace_bytes(tensors, w.M, hp))
+
+        def step(i):
+            hp.step = hp0["step"] + i
+            z.zero_step(tensors, hp, 0.0, ws, res, stream)
 
     for i in range(a.warmup):
         step(i)
@@ -172,13 +190,13 @@ def main():
     per_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(K))
     avg_ms = total_ms / K
     n = w.n_total
-    bpp = w.bytes_per_param()
+    bpp = w.bytes_per_param() if not a.amp else 2 * w.M + 34  # the AMP step is always two-pass
     achieved = bpp * n / (avg_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
         ent = tf.get(str(a.workload))
-        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash():
+        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp:
             traffic = ent["bytes_per_launch"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
@@ -190,7 +208,8 @@ def main():
         "warmup": a.warmup, "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "shard_params": n, "M": w.M, "tensors": len(w.tensors),
-                   "bytes_per_param": bpp, "two_pass": w.two_pass, "step_t": hp0["step"],
+                   "bytes_per_param": bpp, "two_pass": w.two_pass or a.amp, "step_t": hp0["step"],
+                   "loss_scale": "dynamic, on device" if a.amp else "fixed",
                    "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
                    "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4)},
         "roofline": roofline, "cpu_baseline": cpu,
