@@ -103,14 +103,15 @@ int64_t tiles_of(const std::vector<Layout>& layouts, int geom)
 }
 
 // Geometry of the pass that folds the replicas: long per-replica bursts in
-// workgroup lockstep -- 512 threads x 16 vectors (128 KiB of one replica per
-// workgroup, registers to spare for the binary64 update) for a single pass,
-// 1024 x 8 for the first pass of a two-pass step (no update, more waves) --
-// unless the bucket is too small to reach half the compute units.
+// workgroup lockstep -- for a single pass 512 threads x 16 vectors (128 KiB of
+// one replica per workgroup, registers to spare for the binary64 update) when
+// the replica reads dominate (M > 16), else 256 x 16, whose two workgroups
+// per CU overlap one's state update with the other's fold; 1024 x 8 for the
+// first pass of a two-pass step (no update, more waves) -- unless the bucket
+// is too small to reach half the compute units.
 int pick_geom_fold(const std::vector<Layout>& layouts, int M, bool two_pass, int cus)
 {
-    (void)M;
-    const int first = two_pass ? 4 : 5;
+    const int first = two_pass ? 4 : (M > 16 ? 5 : 6);
     if (2 * tiles_of(layouts, first) >= static_cast<int64_t>(cus)) return first;
     for (int g = 3; g > 0; --g)
         if (2 * tiles_of(layouts, g) >= static_cast<int64_t>(cus)) return g;

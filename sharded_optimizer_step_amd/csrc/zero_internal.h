@@ -61,7 +61,7 @@ struct Geom {
     int nt;
     int u;
 };
-constexpr Geom kGeoms[] = {{256, 1}, {1024, 1}, {1024, 2}, {1024, 4}, {1024, 8}, {512, 16}};
+constexpr Geom kGeoms[] = {{256, 1}, {1024, 1}, {1024, 2}, {1024, 4}, {1024, 8}, {512, 16}, {256, 16}};
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 
 // Upper bound of layout_tiles over every alignment of an n-element shard.

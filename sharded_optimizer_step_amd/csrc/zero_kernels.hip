@@ -789,7 +789,8 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
     return hipGetLastError();
 }
 
-#define ZERO_FOR_EACH_GEOM(X) X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8) X(5, 512, 16)
+#define ZERO_FOR_EACH_GEOM(X) \
+    X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8) X(5, 512, 16) X(6, 256, 16)
 
 template <Mode MODE>
 hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map, int64_t tiles,
