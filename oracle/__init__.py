@@ -52,6 +52,11 @@ class _Tensor(ctypes.Structure):
                 ("param_out", ctypes.c_void_p)]
 
 
+class _AccTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grad_acc", ctypes.c_void_p), ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
 class _LossScale(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_float), ("inv_scale", ctypes.c_float), ("good_steps", ctypes.c_int32),
                 ("overflows", ctypes.c_int32)]
@@ -80,6 +85,11 @@ def lib():
         L.oracle_zero_step.argtypes = [ctypes.POINTER(_Tensor), i32, i32, ctypes.POINTER(_Hparams), dbl,
                                        ctypes.POINTER(_Result)]
         L.oracle_zero_step.restype = i32
+        L.oracle_grad_accumulate.argtypes = [ctypes.POINTER(vp), i32, i64, vp, i32]
+        L.oracle_grad_accumulate.restype = None
+        L.oracle_zero_step_accumulated.argtypes = [ctypes.POINTER(_AccTensor), i32, ctypes.POINTER(_Hparams), dbl,
+                                                   ctypes.POINTER(_Result)]
+        L.oracle_zero_step_accumulated.restype = i32
         L.oracle_loss_scale_init.argtypes = [ctypes.POINTER(_LossScaleConfig), ctypes.POINTER(_LossScale)]
         L.oracle_loss_scale_update.argtypes = [ctypes.POINTER(_LossScaleConfig), i32, ctypes.POINTER(_LossScale)]
         L.oracle_loss_scale_init.restype = None
@@ -220,6 +230,53 @@ def zero_step(tensors: Sequence[TensorState], hp: HParams, external_sumsq: float
     rc = lib().oracle_zero_step(cts, T, M, ctypes.byref(h), float(external_sumsq), ctypes.byref(r))
     if rc != 0:
         raise MemoryError("oracle_zero_step: out of host memory")
+    return new, Result(r.sumsq, r.grad_norm, r.clip_coef, r.found_inf, r.skipped)
+
+
+# --------------------------------------------------------------------------
+# ZeRO-2 streaming (see the header of zero_oracle.c): each bucket's replicas
+# are folded into an fp32 shard accumulator as they arrive, micro-batch after
+# micro-batch; the step then runs on g = acc * scale32.
+# --------------------------------------------------------------------------
+
+def grad_accumulate(grads: Sequence[np.ndarray], acc: np.ndarray | None = None) -> np.ndarray:
+    """One micro-batch of one tensor: the binary32 fold of its M bf16
+    replicas, stored (acc None) or added to a copy of acc. Returns the new
+    accumulator; acc is not modified."""
+    gs = [_u16(g) for g in grads]
+    n = gs[0].size
+    assert all(g.size == n for g in gs)
+    ptrs = (ctypes.c_void_p * len(gs))(*[_p(g) for g in gs])
+    out = np.empty(n, np.float32) if acc is None else _f32(acc).copy()
+    assert out.size == n
+    lib().oracle_grad_accumulate(ptrs, len(gs), n, _p(out), 0 if acc is None else 1)
+    return out
+
+
+def zero_step_accumulated(accs: Sequence[np.ndarray], tensors: Sequence[TensorState], hp: HParams,
+                          external_sumsq: float = 0.0):
+    """The step from accumulated fp32 shard gradients accs[t] (the grads of
+    `tensors` are not read). Returns (new TensorStates, Result); the inputs are
+    not modified, and a skipped step returns copies of the old state."""
+    T = len(tensors)
+    assert len(accs) == T
+    cts = (_AccTensor * max(T, 1))()
+    new = []
+    keep = []
+    for i, (a, t) in enumerate(zip(accs, tensors)):
+        a = _f32(a)
+        n = t.master.size
+        assert a.size == n
+        st = TensorState([], _f32(t.master).copy(), _f32(t.exp_avg).copy(), _f32(t.exp_avg_sq).copy(),
+                         (_u16(t.param_out).copy() if t.param_out is not None else np.zeros(n, np.uint16)))
+        keep.append(a)
+        cts[i] = _AccTensor(n, _p(a), _p(st.master), _p(st.exp_avg), _p(st.exp_avg_sq), _p(st.param_out))
+        new.append(st)
+    h = hp._c()
+    r = _Result()
+    rc = lib().oracle_zero_step_accumulated(cts, T, ctypes.byref(h), float(external_sumsq), ctypes.byref(r))
+    if rc != 0:
+        raise MemoryError("oracle_zero_step_accumulated: out of host memory")
     return new, Result(r.sumsq, r.grad_norm, r.clip_coef, r.found_inf, r.skipped)
 
 

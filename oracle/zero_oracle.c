@@ -55,6 +55,19 @@
  *                oracle_loss_scale_update below ([5D post] 4.2 fp16 block,
  *                3.2 trap 3).
  *
+ * ZeRO-2, streaming ([CS336 L7] "ZeRO Stage 2": each layer's gradient is
+ * reduced to the rank that owns it as soon as backward has produced it, so
+ * no rank holds a whole gradient; [5D post] 4.2: gradients travel in buckets
+ * of reduce_bucket_size, over gradient_accumulation_steps micro-batches):
+ *
+ *   1'. accumulate  for each micro-batch k and each tensor of a bucket:
+ *                s = the step-1 fold of that micro-batch's M replicas;
+ *                acc[i] = s (first micro-batch) or acc[i] + s (later ones),
+ *                one binary32 add: the fp32 shard gradient is a running sum
+ *                of reduce-scatter results.
+ *   2'-6'.       the step then runs steps 2-6 on g[i] = acc[i] * scale32.
+ *   With one micro-batch this is exactly the ZeRO-1 step above.
+ *
  * Compile with -O2 -ffp-contract=off and without -ffast-math: the binary32
  * fold of step 1 must be exactly the sequence of rounded adds written here.
  */
@@ -268,6 +281,60 @@ int32_t oracle_zero_step(const oracle_tensor* ts, int32_t T, int32_t M, const or
         gs[t] = (float*)malloc((size_t)(ts[t].n > 0 ? ts[t].n : 1) * sizeof(float));
         if (!gs[t]) { rc = -1; goto done; }
         oracle_reduce(ts[t].grads, M, ts[t].n, hp->grad_scale, gs[t]);
+        oracle_check(gs[t], ts[t].n, &sumsq, &found_inf);
+    }
+    oracle_finalize(sumsq, external_sumsq, found_inf, hp->max_grad_norm, hp->skip_on_nonfinite, res);
+    if (!res->skipped)
+        for (int32_t t = 0; t < T; ++t)
+            oracle_adamw(ts[t].master, ts[t].exp_avg, ts[t].exp_avg_sq, gs[t], ts[t].param_out, ts[t].n, hp,
+                         res->clip_coef);
+done:
+    for (int32_t t = 0; t < T; ++t) free(gs[t]);
+    free(gs);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ZeRO-2 streaming: per-bucket accumulation, then the step from the        */
+/* accumulated fp32 shard gradient.                                         */
+/* ------------------------------------------------------------------------ */
+
+/* One micro-batch of one tensor: fold its M replicas (step 1, without the
+ * scale) and store the fold (accumulate == 0) or add it to acc (binary32). */
+void oracle_grad_accumulate(const uint16_t* const* grads, int32_t M, int64_t n, float* acc, int32_t accumulate)
+{
+    bf16_table_init();
+    for (int64_t i = 0; i < n; ++i) {
+        float s = bf16_to_float(grads[0][i]);
+        for (int32_t r = 1; r < M; ++r) s = s + bf16_to_float(grads[r][i]);
+        acc[i] = accumulate ? acc[i] + s : s;
+    }
+}
+
+typedef struct {
+    int64_t n;
+    const float* grad_acc; /* n fp32: the accumulated (unscaled) shard gradient */
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    uint16_t* param_out;
+} oracle_acc_tensor;
+
+/* Steps 2-6 on g = acc * scale32 over a tensor list. Returns 0, or -1 when
+ * scratch memory cannot be had. */
+int32_t oracle_zero_step_accumulated(const oracle_acc_tensor* ts, int32_t T, const oracle_hparams* hp,
+                                     double external_sumsq, oracle_result* res)
+{
+    float** gs = (float**)calloc((size_t)(T > 0 ? T : 1), sizeof(float*));
+    if (!gs) return -1;
+    const float scale = (float)hp->grad_scale;
+    double sumsq = 0.0;
+    int32_t found_inf = 0;
+    int32_t rc = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        gs[t] = (float*)malloc((size_t)(ts[t].n > 0 ? ts[t].n : 1) * sizeof(float));
+        if (!gs[t]) { rc = -1; goto done; }
+        for (int64_t i = 0; i < ts[t].n; ++i) gs[t][i] = ts[t].grad_acc[i] * scale;
         oracle_check(gs[t], ts[t].n, &sumsq, &found_inf);
     }
     oracle_finalize(sumsq, external_sumsq, found_inf, hp->max_grad_norm, hp->skip_on_nonfinite, res);
