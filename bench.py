@@ -14,6 +14,12 @@ the step kernels (algorithmic bytes / average step duration from HIP events
 on the launch stream), the counter-measured HBM traffic when a profile of the
 current kernel source is on file, and the CPU oracle timed on a bounded
 sample of the same workload.
+
+--zero2 times the ZeRO-2 streaming form instead (default workload: the
+ragged Llama-7B-shaped bucket list): each step reduces every gradient bucket
+(reduce_bucket_size 5e7 elements, backward order) into the fp32 shard
+accumulators with zero_bucket_reduce, for --micro-batches micro-batches,
+then applies zero_step_accumulated.
 """
 from __future__ import annotations
 
@@ -43,12 +49,16 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", type=int, default=2, help="0..4, see synth/workloads.py")
+    p.add_argument("--workload", type=int, default=None,
+                   help="0..4, see synth/workloads.py (default 2; 3 with --zero2)")
     p.add_argument("--cpu-sample", type=int, default=1 << 26,
                    help="elements of the shard the CPU oracle runs on (0: skip the CPU baseline)")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a plain 4 GiB device copy (HBM counter calibration)")
     p.add_argument("--stagger", type=int, default=0, help="bytes added between consecutive replica bases")
+    p.add_argument("--zero2", action="store_true",
+                   help="the ZeRO-2 streaming step: per-bucket zero_bucket_reduce, then zero_step_accumulated")
+    p.add_argument("--micro-batches", type=int, default=1, help="--zero2: micro-batches accumulated per step")
     p.add_argument("--amp", action="store_true",
                    help="step with zero_step_amp: the loss scale held on the device, starting at the workload's "
                         "1/grad_scale (a power of two), window 1000, hysteresis 2")
@@ -129,6 +139,85 @@ def cpu_baseline(w, sample: int) -> dict:
             "sample": f"first {S:,} elements of the shard with all {w.M} replicas ({dt:.1f} s, single thread)"}
 
 
+def zero2_line(a, w, tensors) -> dict:
+    """Times the ZeRO-2 streaming step; returns the fields of the JSON line."""
+    import torch
+
+    import sharded_optimizer_step_amd as z
+    from synth.workloads import zero2_buckets
+
+    K = max(1, a.micro_batches)
+    buckets = zero2_buckets(w)
+    n = w.n_total
+    # one contiguous fp32 accumulator for the whole shard, a view per tensor
+    flat = torch.empty(n, dtype=torch.float32, device="cuda")
+    accs, pos = [], 0
+    for spec in w.tensors:
+        accs.append(flat[pos:pos + spec.n])
+        pos += spec.n
+    parts = z.new_bucket_partials(len(buckets))
+    reducers = [z.BucketReducer([z.GradShard(tensors[t].grads, accs[t]) for t in idx], parts[32 * b:32 * b + 32])
+                for b, idx in enumerate(buckets)]
+    ats = [z.AccTensor(acc, t.master, t.exp_avg, t.exp_avg_sq, t.param_out) for acc, t in zip(accs, tensors)]
+    sws = z.workspace(z.zero_step_accumulated_workspace_bytes(ats))
+    hp0 = w.hparams()
+    hp = z.HParams(**hp0)
+    res = z.new_result()
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        hp.step = hp0["step"] + i
+        stamp = i + 1
+        for k in range(K):
+            flags = (z.BUCKET_ACCUMULATE if k else 0) | (z.BUCKET_FINAL if k == K - 1 else 0)
+            for rd in reducers:
+                rd.reduce(flags, hp.grad_scale, stamp, stream)
+        if ev is not None:
+            ev.record(stream)
+        z.zero_step_accumulated(ats, hp, parts, len(buckets), stamp, 0.0, sws, res, stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    r = z.read_result(res)
+    if r["status"] != 0:
+        raise RuntimeError(f"step status {r}")
+    S = a.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(S + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(S):
+        step(a.warmup + i, mid[i])
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[S])
+    per_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(S))
+    reduce_ms = sum(ev[i].elapsed_time(mid[i]) for i in range(S)) / S
+    update_ms = sum(mid[i].elapsed_time(ev[i + 1]) for i in range(S)) / S
+    avg_ms = total_ms / S
+    # algorithmic bytes per shard parameter: the first micro-batch reads M
+    # replicas and writes the fp32 sum, later ones also read it back; the
+    # step reads g and the state, writes the state and the bf16 shard
+    b_reduce = 2 * w.M * K + 4 + 8 * (K - 1)
+    b_update = 30
+    bpp = b_reduce + b_update
+    dom = ("update", b_update, update_ms) if update_ms >= reduce_ms else ("bucket reduces", b_reduce, reduce_ms)
+    achieved = dom[1] * n / (dom[2] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    cfg = {"workload": w.name + f", ZeRO-2 streaming: {len(buckets)} buckets of reduce_bucket_size 5e7 "
+                                f"in backward order, {K} micro-batch(es)",
+           "shard_params": n, "M": w.M, "tensors": len(w.tensors), "buckets": len(buckets), "micro_batches": K,
+           "bytes_per_param": bpp, "step_t": hp0["step"],
+           "hbm_gbs": round(bpp * n / (avg_ms * 1e-3) / 1e9, 1),
+           "reduce_ms": round(reduce_ms, 4), "reduce_gbs": round(b_reduce * n / (reduce_ms * 1e-3) / 1e9, 1),
+           "update_ms": round(update_ms, 4), "update_gbs": round(b_update * n / (update_ms * 1e-3) / 1e9, 1),
+           "roofline_kernel": dom[0],
+           "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[S // 2], 4)}
+    return {"value": n / (avg_ms * 1e-3), "ms_per_step": avg_ms, "config": cfg, "roofline": roofline}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -144,8 +233,21 @@ def main():
     if a.calib_copy:
         calib_copy(max(a.steps, 1))
         return
+    if a.workload is None:
+        a.workload = 3 if a.zero2 else 2
     w = workload(a.workload)
     tensors = build_workload(w, a.stagger)
+    if a.zero2:
+        if a.amp:
+            sys.exit("bench.py: --zero2 runs with a fixed loss scale")
+        out = zero2_line(a, w, tensors)
+        cpu = cpu_baseline(w, a.cpu_sample) if a.cpu_sample > 0 else None
+        line = {"metric": METRIC, "value": out["value"], "unit": "params/s", "n_gpus": 1, "steps": a.steps,
+                "warmup": a.warmup, "ms_per_step": out["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": out["config"],
+                "roofline": out["roofline"], "cpu_baseline": cpu}
+        print(json.dumps(line), flush=True)
+        return
     hp0 = w.hparams()
     hp = z.HParams(**hp0)
     res = z.new_result()

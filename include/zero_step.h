@@ -70,6 +70,10 @@ extern "C" {
 #define ZERO_ERR_STALE_WORKSPACE 4     /* set in zero_result.status by the device when a
                                           workspace no longer holds the plan of this call;
                                           the step then wrote nothing */
+#define ZERO_ERR_BUCKET_PARTIALS 5     /* set in zero_result.status by zero_step_accumulated
+                                          when a bucket partial was not written by a final
+                                          zero_bucket_reduce with this stamp and grad_scale;
+                                          the step then wrote nothing */
 
 /* Largest M accepted (ranks, i.e. gradient replicas per shard). */
 #define ZERO_MAX_RANKS 65536
@@ -251,9 +255,116 @@ int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_a
                   const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, double external_sumsq, void* ws,
                   size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * ZeRO-2, streaming.
+ *
+ * "CS336 Lecture 7: Parallelism 1", section "ZeRO Stage 2": as backward
+ * produces each layer's gradient, it is reduced at once to the rank that owns
+ * its shard, and the local copy is freed, so no rank holds a whole gradient.
+ * gsyq.cn/news/457874 section 4.2 sends gradients in buckets
+ * (reduce_bucket_size) and accumulates gradient_accumulation_steps
+ * micro-batches per step. At one rank, on one GPU:
+ *   - zero_bucket_reduce, once per bucket and micro-batch, as the bucket's M
+ *     replicas arrive: acc[i] = fold(replicas) for the first micro-batch, or
+ *     acc[i] = acc[i] + fold(replicas) (one binary32 add) for later ones. The
+ *     fold is zero_shard_reduce's, without the scale: acc is the running sum
+ *     of the reduce-scatter results. On the last micro-batch (FINAL) the call
+ *     also writes the bucket's sum of squares and non-finite flag of
+ *     g = acc * fl32(grad_scale) to a 32-byte bucket partial, stamped;
+ *   - zero_step_accumulated, once per step: combines the bucket partials in
+ *     index order into the result record (norm, clip coefficient, skip), then
+ *     applies AdamW and the bf16 emit from g = acc * fl32(grad_scale), as
+ *     zero_step does from its fold.
+ * With one micro-batch, the state this writes is bit-identical to zero_step's
+ * over the same replicas when clipping is off (the norm's summation tree
+ * differs, so a clipped step may differ by the last bit of the coefficient).
+ * ------------------------------------------------------------------------ */
+
+/* flags of zero_bucket_reduce */
+#define ZERO_BUCKET_ACCUMULATE 1 /* add the fold to acc; otherwise store it (first micro-batch) */
+#define ZERO_BUCKET_FINAL 2      /* last micro-batch of the step: also write the bucket partial */
+
+/* One tensor shard of a gradient bucket. Host memory. */
+typedef struct zero_grad_shard {
+    int64_t n;                /* elements in this shard, >= 0 */
+    const void* const* grads; /* HOST array of M device pointers, n bf16 each (read only) */
+    float* grad_acc;          /* device, n fp32: the shard's accumulated gradient, updated */
+} zero_grad_shard;
+
+/* One bucket's share of the step's norm and flag, 32 bytes, device memory. */
+typedef struct zero_bucket_partial {
+    double sumsq;      /* sum over the bucket of g^2, g = acc * fl32(grad_scale) (binary64) */
+    uint64_t stamp;    /* the stamp of the final zero_bucket_reduce that wrote it */
+    int32_t found_inf; /* 1 when any g of the bucket is inf or NaN */
+    float grad_scale;  /* fl32(grad_scale) of that call */
+    int64_t reserved;  /* written 0 */
+} zero_bucket_partial;
+
+/* One tensor shard of a zero_step_accumulated list. Host memory. */
+typedef struct zero_acc_tensor {
+    int64_t n;              /* elements in this shard, >= 0 */
+    const float* grad_acc;  /* device, n fp32: the accumulated gradient (read only) */
+    float* master;          /* device, n fp32, updated in place */
+    float* exp_avg;         /* device, n fp32, updated in place */
+    float* exp_avg_sq;      /* device, n fp32, updated in place */
+    void* param_out;        /* device, n bf16 codes, written */
+} zero_acc_tensor;
+
+/*
+ * zero_bucket_reduce_workspace_bytes -- workspace size for zero_bucket_reduce
+ * over this bucket (pointers inside `shards` are not read); 0 on invalid
+ * arguments.
+ */
+size_t zero_bucket_reduce_workspace_bytes(const zero_grad_shard* shards, int32_t T, int32_t M);
+
+/*
+ * zero_bucket_reduce -- fold one micro-batch of one bucket (T tensor shards,
+ * M bf16 replicas each) into the shards' fp32 accumulators, per `flags`
+ * (ZERO_BUCKET_ACCUMULATE, ZERO_BUCKET_FINAL; other bits are an error).
+ * With ZERO_BUCKET_FINAL, grad_scale (finite, > 0; the step's) and stamp (any
+ * value that differs from the previous step's, e.g. an iteration count) go
+ * into *partial_dev (device, 32 bytes); without it they are ignored and
+ * partial_dev may be NULL. ws: device workspace of
+ * zero_bucket_reduce_workspace_bytes(...) bytes, 256-byte aligned, one per
+ * bucket (it caches the bucket's tables; calls that share one must not run
+ * concurrently). A workspace that no longer holds this bucket's tables is
+ * detected on the device: nothing is written but *partial_dev, whose stamp is
+ * then invalid (zero_step_accumulated reports it; a later final call on a
+ * valid workspace would overwrite it, so call zero_workspace_forget before
+ * reusing a bucket workspace for anything else). The accumulators must not
+ * overlap the replicas or each other.
+ */
+int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                       uint64_t stamp, zero_bucket_partial* partial_dev, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * zero_step_accumulated_workspace_bytes -- workspace size for
+ * zero_step_accumulated over this tensor list; 0 on invalid arguments.
+ */
+size_t zero_step_accumulated_workspace_bytes(const zero_acc_tensor* tensors, int32_t T);
+
+/*
+ * zero_step_accumulated -- the step from the accumulated shard gradients:
+ * partials_dev (device, nbuckets >= 0 records, each written by the final
+ * zero_bucket_reduce of one bucket with this `stamp` and hp->grad_scale) are
+ * combined in index order, with external_sumsq, into res_dev (norm, clip
+ * coefficient, skip, as zero_step); unless skipped, AdamW and the bf16 emit
+ * are applied to every tensor from g = acc * fl32(hp->grad_scale). A partial
+ * with another stamp or scale sets res_dev->status = ZERO_ERR_BUCKET_PARTIALS
+ * and nothing is written. ws: device workspace of
+ * zero_step_accumulated_workspace_bytes(...) bytes, 256-byte aligned, as for
+ * zero_step.
+ */
+int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                          const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                          double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
+                          hipStream_t stream);
+
 /*
  * zero_workspace_forget -- drop the host-side record that `ws` holds the
- * tensor table of an earlier zero_step call. Call it before freeing or
+ * tensor table of an earlier zero_step, zero_step_amp, zero_bucket_reduce or
+ * zero_step_accumulated call. Call it before freeing or
  * repurposing such a workspace; the next zero_step on it then rewrites the
  * table. (A workspace whose table was overwritten without this call is
  * detected on the device: zero_result.status = ZERO_ERR_STALE_WORKSPACE and

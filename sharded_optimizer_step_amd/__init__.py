@@ -14,6 +14,12 @@ Functions keep the C names:
 * ``zero_adamw_step(master, exp_avg, exp_avg_sq, g, param_out, hp, res=None)``
 * ``zero_step_workspace_bytes(tensors, M, hp)``
 * ``zero_step(tensors, hp, external_sumsq, ws, res)``
+* ``zero_loss_scale_init(cfg, ls)``, ``zero_loss_scale_update(cfg, res, ls)``
+* ``zero_step_amp_workspace_bytes(tensors, M, hp)``, ``zero_step_amp(tensors, hp, cfg, ls, external_sumsq, ws, res)``
+* ``zero_bucket_reduce_workspace_bytes(shards, M)``,
+  ``zero_bucket_reduce(shards, flags, grad_scale, stamp, partial, ws)``
+* ``zero_step_accumulated_workspace_bytes(tensors)``,
+  ``zero_step_accumulated(tensors, hp, partials, stamp, external_sumsq, ws, res)``
 * ``zero_workspace_forget(ws)``, ``zero_status_string(status)``
 """
 from __future__ import annotations
@@ -35,12 +41,18 @@ ZERO_ERR_INVALID_ARGUMENT = 1
 ZERO_ERR_WORKSPACE_TOO_SMALL = 2
 ZERO_ERR_HIP = 3
 ZERO_ERR_STALE_WORKSPACE = 4
+ZERO_ERR_BUCKET_PARTIALS = 5
 RESULT_BYTES = 32
+BUCKET_ACCUMULATE = 1
+BUCKET_FINAL = 2
+BUCKET_PARTIAL_BYTES = 32
 
 # Every symbol the C ABI exports (include/zero_step.h).
 EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_grad_check_norm", "zero_adamw_step",
            "zero_step_workspace_bytes", "zero_step", "zero_loss_scale_init", "zero_loss_scale_update",
-           "zero_step_amp_workspace_bytes", "zero_step_amp", "zero_workspace_forget", "zero_status_string")
+           "zero_step_amp_workspace_bytes", "zero_step_amp", "zero_bucket_reduce_workspace_bytes",
+           "zero_bucket_reduce", "zero_step_accumulated_workspace_bytes", "zero_step_accumulated",
+           "zero_workspace_forget", "zero_status_string")
 LOSS_SCALE_BYTES = 16
 
 
@@ -53,6 +65,15 @@ class _CHparams(ctypes.Structure):
 
 class _CTensor(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class _CGradShard(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("grad_acc", ctypes.c_void_p)]
+
+
+class _CAccTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grad_acc", ctypes.c_void_p), ("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
 
 
@@ -100,6 +121,16 @@ def lib() -> ctypes.CDLL:
         L.zero_step_amp.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams),
                                     ctypes.POINTER(_CLossScaleConfig), vp, dbl, vp, sz, vp, vp]
         L.zero_step_amp.restype = ctypes.c_int
+        u64 = ctypes.c_uint64
+        L.zero_bucket_reduce_workspace_bytes.argtypes = [ctypes.POINTER(_CGradShard), i32, i32]
+        L.zero_bucket_reduce_workspace_bytes.restype = sz
+        L.zero_bucket_reduce.argtypes = [ctypes.POINTER(_CGradShard), i32, i32, i32, dbl, u64, vp, vp, sz, vp]
+        L.zero_bucket_reduce.restype = ctypes.c_int
+        L.zero_step_accumulated_workspace_bytes.argtypes = [ctypes.POINTER(_CAccTensor), i32]
+        L.zero_step_accumulated_workspace_bytes.restype = sz
+        L.zero_step_accumulated.argtypes = [ctypes.POINTER(_CAccTensor), i32, ctypes.POINTER(_CHparams), vp, i32,
+                                            u64, dbl, vp, sz, vp, vp]
+        L.zero_step_accumulated.restype = ctypes.c_int
         L.zero_workspace_forget.argtypes = [vp]
         L.zero_workspace_forget.restype = ctypes.c_int
         L.zero_status_string.argtypes = [ctypes.c_int]
@@ -315,6 +346,135 @@ def zero_step_amp(tensors: Sequence[ZeroTensor], hp: HParams, cfg: LossScaleConf
     _check(lib().zero_step_amp(arr, len(tensors), M, ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
                                float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
            "zero_step_amp")
+
+
+# ---------------------------------------------------------------- ZeRO-2 streaming
+
+@dataclasses.dataclass
+class GradShard:
+    """One tensor shard of a gradient bucket: M bf16 replicas of this
+    micro-batch and the shard's fp32 gradient accumulator."""
+    grads: List[torch.Tensor]
+    grad_acc: torch.Tensor
+
+
+@dataclasses.dataclass
+class AccTensor:
+    """One tensor shard of the step from accumulated gradients."""
+    grad_acc: torch.Tensor
+    master: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    param_out: torch.Tensor
+
+
+def new_bucket_partials(nbuckets: int, device=None) -> torch.Tensor:
+    """Device storage for nbuckets zero_bucket_partial records (32 bytes each)."""
+    return torch.zeros(max(nbuckets, 1) * BUCKET_PARTIAL_BYTES, dtype=torch.uint8, device=device or "cuda")
+
+
+def read_bucket_partial(partials: torch.Tensor, index: int = 0) -> dict:
+    """Copy one bucket partial to the host (synchronizes with its stream)."""
+    b = bytes(partials[index * BUCKET_PARTIAL_BYTES:(index + 1) * BUCKET_PARTIAL_BYTES].cpu().numpy().tobytes())
+    sumsq, stamp, found_inf, scale, reserved = struct.unpack("<dQifq", b)
+    return dict(sumsq=sumsq, stamp=stamp, found_inf=found_inf, grad_scale=scale, reserved=reserved)
+
+
+def _cshards(shards: Sequence[GradShard], check: bool):
+    M = len(shards[0].grads) if shards else 1
+    keep = []
+    arr = (_CGradShard * max(len(shards), 1))()
+    for i, t in enumerate(shards):
+        n = t.grad_acc.numel()
+        if check:
+            if len(t.grads) != M:
+                raise ValueError(f"shard {i}: {len(t.grads)} replicas, expected {M}")
+            for r, g in enumerate(t.grads):
+                _need(g, torch.bfloat16, f"shards[{i}].grads[{r}]", n)
+            _need(t.grad_acc, torch.float32, f"shards[{i}].grad_acc", n)
+        ptrs = (ctypes.c_void_p * max(M, 1))(*[g.data_ptr() for g in t.grads])
+        keep.append(ptrs)
+        arr[i] = _CGradShard(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), t.grad_acc.data_ptr())
+    return arr, keep, M
+
+
+def zero_bucket_reduce_workspace_bytes(shards: Sequence[GradShard], M: int) -> int:
+    arr, keep, _ = _cshards(shards, check=False)
+    return int(lib().zero_bucket_reduce_workspace_bytes(arr, len(shards), int(M)))
+
+
+def zero_bucket_reduce(shards: Sequence[GradShard], flags: int, grad_scale: float, stamp: int,
+                       partial: Optional[torch.Tensor], ws: Optional[torch.Tensor], stream=None) -> None:
+    """partial: a 32-byte slice of new_bucket_partials(...) (this bucket's
+    record), required with BUCKET_FINAL."""
+    if partial is not None:
+        _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
+    arr, keep, M = _cshards(shards, check=True)
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_bucket_reduce(arr, len(shards), M, int(flags), float(grad_scale), int(stamp) & (2**64 - 1),
+                                    _ptr(partial), _ptr(ws), wsb, _stream(stream)), "zero_bucket_reduce")
+
+
+class BucketReducer:
+    """One gradient bucket marshalled once, for a training loop that reduces
+    it every micro-batch: reduce() calls zero_bucket_reduce with the arguments
+    prepared here and no per-call Python checks. The shards' tensors, the
+    partial and the workspace must stay alive and at the same addresses."""
+
+    def __init__(self, shards: Sequence[GradShard], partial: Optional[torch.Tensor], ws: Optional[torch.Tensor] = None):
+        self._arr, self._keep, self.M = _cshards(shards, check=True)
+        self._shards = list(shards)
+        self.T = len(self._shards)
+        if partial is not None:
+            _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
+        self._partial = partial
+        if ws is None:
+            ws = workspace(zero_bucket_reduce_workspace_bytes(self._shards, self.M))
+        self.ws = ws
+        self._wsp = _ptr(ws)
+        self._wsb = ws.numel() * ws.element_size() if ws is not None else 0
+        self._pp = _ptr(partial)
+        self._fn = lib().zero_bucket_reduce
+
+    def reduce(self, flags: int, grad_scale: float, stamp: int, stream=None) -> None:
+        st = self._fn(self._arr, self.T, self.M, flags, grad_scale, stamp & 0xFFFFFFFFFFFFFFFF, self._pp, self._wsp,
+                      self._wsb, _stream(stream))
+        if st != ZERO_OK:
+            raise ZeroError(st, "zero_bucket_reduce")
+
+
+def _cacc(tensors: Sequence[AccTensor], check: bool):
+    arr = (_CAccTensor * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        n = t.master.numel()
+        if check:
+            for x, nm in ((t.grad_acc, "grad_acc"), (t.master, "master"), (t.exp_avg, "exp_avg"),
+                          (t.exp_avg_sq, "exp_avg_sq")):
+                _need(x, torch.float32, f"tensors[{i}].{nm}", n)
+            _need(t.param_out, torch.bfloat16, f"tensors[{i}].param_out", n)
+        arr[i] = _CAccTensor(n, t.grad_acc.data_ptr(), t.master.data_ptr(), t.exp_avg.data_ptr(),
+                             t.exp_avg_sq.data_ptr(), t.param_out.data_ptr())
+    return arr
+
+
+def zero_step_accumulated_workspace_bytes(tensors: Sequence[AccTensor]) -> int:
+    return int(lib().zero_step_accumulated_workspace_bytes(_cacc(tensors, check=False), len(tensors)))
+
+
+def zero_step_accumulated(tensors: Sequence[AccTensor], hp: HParams, partials: Optional[torch.Tensor], nbuckets: int,
+                          stamp: int, external_sumsq: float, ws: Optional[torch.Tensor], res: torch.Tensor,
+                          stream=None) -> None:
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    if nbuckets > 0:
+        _need(partials, torch.uint8, "partials")
+        if partials.numel() < nbuckets * BUCKET_PARTIAL_BYTES:
+            raise ValueError(f"partials: {partials.numel()} bytes for {nbuckets} buckets")
+    arr = _cacc(tensors, check=True)
+    h = hp._c()
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_step_accumulated(arr, len(tensors), ctypes.byref(h), _ptr(partials), int(nbuckets),
+                                       int(stamp) & (2**64 - 1), float(external_sumsq), _ptr(ws), wsb,
+                                       res.data_ptr(), _stream(stream)), "zero_step_accumulated")
 
 
 def zero_workspace_forget(ws: torch.Tensor) -> None:

@@ -129,22 +129,27 @@ int pick_geom_update(const std::vector<Layout>& layouts, int cus)
 
 // ------------------------------------------------------------------ plans
 
-PlanOffsets plan_offsets(const zero_tensor* ts, int32_t T, int32_t M, bool two_pass)
+bool kind_folds(PlanKind k) { return k != PlanKind::AccStep; }
+bool kind_updates_after(PlanKind k) { return k == PlanKind::StepTwoPass || k == PlanKind::AccStep; }
+
+PlanOffsets plan_offsets(const std::vector<int64_t>& ns, int32_t M, PlanKind kind)
 {
     PlanOffsets o{};
+    const size_t T = ns.size();
     int64_t tiles = 0;  // bound over every geometry (the smallest tile is kTileElems)
     size_t gbytes = 0;
-    for (int32_t t = 0; t < T; ++t) {
-        tiles += tiles_bound(ts[t].n);
-        if (two_pass && ts[t].n > 0) gbytes += align_up((static_cast<size_t>(ts[t].n) + 3) * 4, kAlign);
+    for (int64_t n : ns) {
+        tiles += tiles_bound(n);
+        if (kind == PlanKind::StepTwoPass && n > 0) gbytes += align_up((static_cast<size_t>(n) + 3) * 4, kAlign);
     }
     const size_t ntiles = static_cast<size_t>(tiles);
+    const bool folds = kind_folds(kind);
     o.desc = kAlign;
-    o.ptrs = align_up(o.desc + sizeof(TensorDesc) * static_cast<size_t>(T), kAlign);
-    o.map0 = align_up(o.ptrs + sizeof(void*) * static_cast<size_t>(T) * static_cast<size_t>(M), kAlign);
-    o.map1 = align_up(o.map0 + sizeof(TileRef) * ntiles, kAlign);
-    o.parts = align_up(o.map1 + (two_pass ? sizeof(TileRef) * ntiles : 0), kAlign);
-    o.gbuf = align_up(o.parts + sizeof(Partial) * ntiles, kAlign);
+    o.ptrs = align_up(o.desc + sizeof(TensorDesc) * T, kAlign);
+    o.map0 = align_up(o.ptrs + (folds ? sizeof(void*) * T * static_cast<size_t>(M) : 0), kAlign);
+    o.map1 = align_up(o.map0 + (folds ? sizeof(TileRef) * ntiles : 0), kAlign);
+    o.parts = align_up(o.map1 + (kind_updates_after(kind) ? sizeof(TileRef) * ntiles : 0), kAlign);
+    o.gbuf = align_up(o.parts + (folds ? sizeof(Partial) * ntiles : 0), kAlign);
     o.total = o.gbuf + gbytes;
     return o;
 }
@@ -170,6 +175,234 @@ void forget_ws(const void* ws)
     }
 }
 
+// One tensor of a plan: the M replica pointers of the passes that fold them,
+// the state and output of the passes that update, and the caller's fp32
+// gradient buffer of the bucket and accumulated-step plans.
+struct PlanTensor {
+    int64_t n = 0;
+    const void* const* grads = nullptr;
+    float* master = nullptr;
+    float* m = nullptr;
+    float* v = nullptr;
+    void* out = nullptr;
+    float* acc = nullptr;
+};
+
+struct Plan {
+    PlanOffsets off;
+    int geom[2];
+    int64_t tiles[2];
+    uint64_t sig;
+    PlanHeader* hdr;
+    TensorDesc* desc;
+    TileRef* map0;
+    TileRef* map1;
+    Partial* parts;
+    unsigned* counter;
+};
+
+// Builds the plan of `kind` for these tensors in `ws` (tables, tile maps,
+// header with its signature), uploading it unless the workspace already
+// holds it. Returns a status.
+int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void* ws, size_t ws_bytes,
+              hipStream_t stream, Plan* plan)
+{
+    if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    const int32_t T = static_cast<int32_t>(ts.size());
+    std::vector<int64_t> ns;
+    for (const PlanTensor& x : ts) ns.push_back(x.n);
+    const bool folds = kind_folds(kind), updates = kind_updates_after(kind);
+    const PlanOffsets off = plan_offsets(ns, M, kind);
+    if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+
+    // ---- header, tensor table, rank-pointer table (host image)
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    std::vector<uint8_t> blob(off.map0, 0);
+    PlanHeader* hdr = reinterpret_cast<PlanHeader*>(blob.data());
+    TensorDesc* desc = reinterpret_cast<TensorDesc*>(blob.data() + off.desc);
+    const uint16_t** ptrs = reinterpret_cast<const uint16_t**>(blob.data() + off.ptrs);
+    std::vector<Layout> layouts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const PlanTensor& x = ts[t];
+        if (x.n == 0) {
+            layouts[t] = Layout{0, -1, 0, 0};
+            continue;
+        }
+        std::vector<uintptr_t> b16, f32;
+        if (folds)
+            for (int32_t r = 0; r < M; ++r) b16.push_back(reinterpret_cast<uintptr_t>(x.grads[r]));
+        if (x.out) b16.push_back(reinterpret_cast<uintptr_t>(x.out));
+        for (const float* p : {x.acc, x.master, x.m, x.v})
+            if (p) f32.push_back(reinterpret_cast<uintptr_t>(p));
+        layouts[t] = make_layout(x.n, b16, f32);
+    }
+    const int cus = compute_units();
+    const int geom[2] = {folds ? pick_geom_fold(layouts, M, kind != PlanKind::Step, cus) : 0,
+                         updates ? pick_geom_update(layouts, cus) : 0};
+    const int64_t tile_vecs[2] = {static_cast<int64_t>(kGeoms[geom[0]].nt) * kGeoms[geom[0]].u,
+                                  static_cast<int64_t>(kGeoms[geom[1]].nt) * kGeoms[geom[1]].u};
+    int64_t tiles[2] = {0, 0};
+    size_t gpos = off.gbuf;
+    for (int32_t t = 0; t < T; ++t) {
+        const PlanTensor& x = ts[t];
+        TensorDesc& d = desc[t];
+        d.grads = folds ? reinterpret_cast<const uint16_t* const*>(wsb + off.ptrs + sizeof(void*) * static_cast<size_t>(t) * M)
+                        : nullptr;
+        d.n = x.n;
+        for (int p = 0; p < 2; ++p) d.tile_begin[p] = tiles[p];
+        if (x.n == 0) {
+            d.nvec = -1;
+            continue;
+        }
+        if (folds)
+            for (int32_t r = 0; r < M; ++r)
+                ptrs[static_cast<size_t>(t) * M + r] = static_cast<const uint16_t*>(x.grads[r]);
+        const Layout& L = layouts[t];
+        d.master = x.master;
+        d.exp_avg = x.m;
+        d.exp_avg_sq = x.v;
+        d.out = static_cast<uint16_t*>(x.out);
+        d.nvec = L.nvec;
+        d.head = L.head;
+        d.tail = L.tail;
+        d.ntiles[0] = folds ? layout_tiles(L, tile_vecs[0]) : 0;
+        d.ntiles[1] = updates ? layout_tiles(L, tile_vecs[1]) : 0;
+        if (kind == PlanKind::StepTwoPass) {
+            // aligned with the other pointers at element `head`
+            const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
+            d.gbuf = reinterpret_cast<float*>(wsb + gpos + shift);
+            gpos += align_up((static_cast<size_t>(x.n) + 3) * 4, kAlign);
+        } else {
+            d.gbuf = x.acc;
+        }
+        for (int p = 0; p < 2; ++p) tiles[p] += d.ntiles[p];
+    }
+    hdr->tiles[0] = tiles[0];
+    hdr->tiles[1] = tiles[1];
+    hdr->T = T;
+    hdr->M = M;
+    hdr->geom[0] = geom[0];
+    hdr->geom[1] = geom[1];
+    hdr->two_pass = kind == PlanKind::StepTwoPass ? 1 : 0;
+    hdr->kind = static_cast<int32_t>(kind);
+    uint64_t sig = fnv1a(blob.data(), blob.size(), 1469598103934665603ull);
+    const uintptr_t wsaddr = reinterpret_cast<uintptr_t>(ws);
+    sig = fnv1a(reinterpret_cast<const uint8_t*>(&wsaddr), sizeof(wsaddr), sig);
+    if (sig == 0) sig = 1;
+    hdr->signature = sig;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
+    const auto key = std::make_pair(dev, wsaddr);
+    bool cached;
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        auto it = g_plan_cache.find(key);
+        cached = it != g_plan_cache.end() && it->second == sig;
+    }
+    plan->off = off;
+    plan->geom[0] = geom[0];
+    plan->geom[1] = geom[1];
+    plan->tiles[0] = tiles[0];
+    plan->tiles[1] = tiles[1];
+    plan->sig = sig;
+    plan->hdr = reinterpret_cast<PlanHeader*>(wsb);
+    plan->desc = reinterpret_cast<TensorDesc*>(wsb + off.desc);
+    plan->map0 = folds ? reinterpret_cast<TileRef*>(wsb + off.map0) : nullptr;
+    plan->map1 = updates ? reinterpret_cast<TileRef*>(wsb + off.map1) : nullptr;
+    plan->parts = folds ? reinterpret_cast<Partial*>(wsb + off.parts) : nullptr;
+    plan->counter = reinterpret_cast<unsigned*>(wsb + kCounterOffset);
+    if (!cached) {
+        // tables first, tile maps next, header (with the signature) last
+        WriteChunk c;
+        const size_t bytes_per = sizeof(c.data);
+        for (size_t pos = off.desc; pos < blob.size(); pos += bytes_per) {
+            const size_t len = (blob.size() - pos) < bytes_per ? (blob.size() - pos) : bytes_per;
+            c.offset = pos;
+            c.words = static_cast<uint32_t>(len / 4);
+            c.pad = 0;
+            std::memcpy(c.data, blob.data() + pos, len);
+            if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
+        }
+        if (launch_plan_tiles(plan->desc, T, plan->map0, plan->map1, stream) != hipSuccess) return ZERO_ERR_HIP;
+        c.offset = 0;
+        c.words = static_cast<uint32_t>(off.desc / 4);
+        c.pad = 0;
+        std::memcpy(c.data, blob.data(), off.desc);
+        if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        g_plan_cache[key] = sig;
+    }
+    return ZERO_OK;
+}
+
+std::vector<int64_t> sizes_of(const zero_tensor* ts, int32_t T)
+{
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) ns.push_back(ts[t].n);
+    return ns;
+}
+
+// The fused step; `ls` (with its config `lscfg`) non-null for the AMP form:
+// always two-pass, always skipping on a non-finite gradient, the multiplier
+// read from the device state, which the fold's last workgroup then moves.
+int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
+              void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream,
+              const zero_loss_scale_config* lscfg, zero_loss_scale* ls)
+{
+    // ---- arguments
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr)
+        return ZERO_ERR_INVALID_ARGUMENT;
+    if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    int64_t total_n = 0;
+    std::vector<PlanTensor> pts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_tensor& x = tensors[t];
+        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t] = PlanTensor{x.n, x.grads, x.master, x.exp_avg, x.exp_avg_sq, x.param_out, nullptr};
+        total_n += x.n;
+    }
+    const bool amp = ls != nullptr;
+    const bool two_pass = amp || two_pass_of(hp);
+    const int skip = amp || hp->skip_on_nonfinite != 0;
+    if (total_n == 0) {
+        hipError_t e = launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, stream);
+        if (e == hipSuccess && amp) e = launch_loss_scale_update(*lscfg, res_dev, ls, stream);
+        return hip_status(e);
+    }
+    Plan plan;
+    const int st = make_plan(pts, M, two_pass ? PlanKind::StepTwoPass : PlanKind::Step, ws, ws_bytes, stream, &plan);
+    if (st != ZERO_OK) return st;
+
+    // ---- the step
+    const AdamScalars c = derive(hp);
+    const float gscale = static_cast<float>(hp->grad_scale);
+    const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
+    FinalizeArgs fin{};
+    fin.res = res_dev;
+    fin.counter = plan.counter;
+    fin.external = external_sumsq;
+    fin.max_norm = hp->max_grad_norm;
+    fin.skip = skip;
+    fin.ls = ls;
+    if (amp) fin.lscfg = *lscfg;
+    hipError_t e = launch_fused(first_mode, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
+                                gscale, c, plan.parts, fin, nullptr, stream);
+    if (e != hipSuccess) return ZERO_ERR_HIP;
+    if (two_pass) {
+        // the stored gradient is already scaled
+        e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, M, 1.0f,
+                         c, plan.parts, fin, res_dev, stream);
+        if (e != hipSuccess) return ZERO_ERR_HIP;
+    }
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,6 +415,7 @@ const char* zero_status_string(int status)
     case ZERO_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case ZERO_ERR_HIP: return "HIP runtime error";
     case ZERO_ERR_STALE_WORKSPACE: return "workspace no longer holds the plan of this call";
+    case ZERO_ERR_BUCKET_PARTIALS: return "a bucket partial was not written by a final bucket reduce of this step";
     default: return "unknown status";
     }
 }
@@ -260,163 +494,7 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
     if (T > 0 && tensors == nullptr) return 0;
     for (int32_t t = 0; t < T; ++t)
         if (tensors[t].n < 0) return 0;
-    return plan_offsets(tensors, T, M, two_pass_of(hp)).total;
-}
-
-// The fused step; `ls` (with its config `lscfg`) non-null for the AMP form:
-// always two-pass, always skipping on a non-finite gradient, the multiplier
-// read from the device state, which the fold's last workgroup then moves.
-static int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
-                     void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream,
-                     const zero_loss_scale_config* lscfg, zero_loss_scale* ls)
-{
-    // ---- arguments
-    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr)
-        return ZERO_ERR_INVALID_ARGUMENT;
-    if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
-    int64_t total_n = 0;
-    for (int32_t t = 0; t < T; ++t) {
-        const zero_tensor& x = tensors[t];
-        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
-        if (x.n == 0) continue;
-        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
-        for (int32_t r = 0; r < M; ++r)
-            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
-        total_n += x.n;
-    }
-    const bool amp = ls != nullptr;
-    const bool two_pass = amp || two_pass_of(hp);
-    const int skip = amp || hp->skip_on_nonfinite != 0;
-    if (total_n == 0) {
-        hipError_t e = launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, res_dev, stream);
-        if (e == hipSuccess && amp) e = launch_loss_scale_update(*lscfg, res_dev, ls, stream);
-        return hip_status(e);
-    }
-    if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
-    const PlanOffsets off = plan_offsets(tensors, T, M, two_pass);
-    if (ws_bytes < off.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
-
-    // ---- the plan: header, tensor table, rank-pointer table (host image)
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
-    std::vector<uint8_t> blob(off.map0, 0);
-    PlanHeader* hdr = reinterpret_cast<PlanHeader*>(blob.data());
-    TensorDesc* desc = reinterpret_cast<TensorDesc*>(blob.data() + off.desc);
-    const uint16_t** ptrs = reinterpret_cast<const uint16_t**>(blob.data() + off.ptrs);
-    std::vector<Layout> layouts(static_cast<size_t>(T));
-    for (int32_t t = 0; t < T; ++t) {
-        const zero_tensor& x = tensors[t];
-        if (x.n == 0) {
-            layouts[t] = Layout{0, -1, 0, 0};
-            continue;
-        }
-        std::vector<uintptr_t> b16, f32;
-        for (int32_t r = 0; r < M; ++r) b16.push_back(reinterpret_cast<uintptr_t>(x.grads[r]));
-        b16.push_back(reinterpret_cast<uintptr_t>(x.param_out));
-        f32 = {reinterpret_cast<uintptr_t>(x.master), reinterpret_cast<uintptr_t>(x.exp_avg),
-               reinterpret_cast<uintptr_t>(x.exp_avg_sq)};
-        layouts[t] = make_layout(x.n, b16, f32);
-    }
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ZERO_ERR_HIP;
-    const int cus = compute_units();
-    const int geom[2] = {pick_geom_fold(layouts, M, two_pass, cus), two_pass ? pick_geom_update(layouts, cus) : 0};
-    const int64_t tile_vecs[2] = {static_cast<int64_t>(kGeoms[geom[0]].nt) * kGeoms[geom[0]].u,
-                                  static_cast<int64_t>(kGeoms[geom[1]].nt) * kGeoms[geom[1]].u};
-    int64_t tiles[2] = {0, 0};
-    size_t gpos = off.gbuf;
-    for (int32_t t = 0; t < T; ++t) {
-        const zero_tensor& x = tensors[t];
-        TensorDesc& d = desc[t];
-        d.grads = reinterpret_cast<const uint16_t* const*>(wsb + off.ptrs + sizeof(void*) * static_cast<size_t>(t) * M);
-        d.n = x.n;
-        for (int p = 0; p < 2; ++p) d.tile_begin[p] = tiles[p];
-        if (x.n == 0) {
-            d.nvec = -1;
-            continue;
-        }
-        for (int32_t r = 0; r < M; ++r)
-            ptrs[static_cast<size_t>(t) * M + r] = static_cast<const uint16_t*>(x.grads[r]);
-        const Layout& L = layouts[t];
-        d.master = x.master;
-        d.exp_avg = x.exp_avg;
-        d.exp_avg_sq = x.exp_avg_sq;
-        d.out = static_cast<uint16_t*>(x.param_out);
-        d.nvec = L.nvec;
-        d.head = L.head;
-        d.tail = L.tail;
-        d.ntiles[0] = layout_tiles(L, tile_vecs[0]);
-        d.ntiles[1] = two_pass ? layout_tiles(L, tile_vecs[1]) : 0;
-        if (two_pass) {
-            // aligned with the other pointers at element `head`
-            const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
-            d.gbuf = reinterpret_cast<float*>(wsb + gpos + shift);
-            gpos += align_up((static_cast<size_t>(x.n) + 3) * 4, kAlign);
-        }
-        for (int p = 0; p < 2; ++p) tiles[p] += d.ntiles[p];
-    }
-    hdr->tiles[0] = tiles[0];
-    hdr->tiles[1] = tiles[1];
-    hdr->T = T;
-    hdr->M = M;
-    hdr->geom[0] = geom[0];
-    hdr->geom[1] = geom[1];
-    hdr->two_pass = two_pass ? 1 : 0;
-    uint64_t sig = fnv1a(blob.data(), blob.size(), 1469598103934665603ull);
-    const uintptr_t wsaddr = reinterpret_cast<uintptr_t>(ws);
-    sig = fnv1a(reinterpret_cast<const uint8_t*>(&wsaddr), sizeof(wsaddr), sig);
-    if (sig == 0) sig = 1;
-    hdr->signature = sig;
-
-    const auto key = std::make_pair(dev, wsaddr);
-    bool cached;
-    {
-        std::lock_guard<std::mutex> lk(g_plan_mu);
-        auto it = g_plan_cache.find(key);
-        cached = it != g_plan_cache.end() && it->second == sig;
-    }
-    PlanHeader* hdr_dev = reinterpret_cast<PlanHeader*>(wsb);
-    TensorDesc* desc_dev = reinterpret_cast<TensorDesc*>(wsb + off.desc);
-    TileRef* map0 = reinterpret_cast<TileRef*>(wsb + off.map0);
-    TileRef* map1 = two_pass ? reinterpret_cast<TileRef*>(wsb + off.map1) : nullptr;
-    Partial* parts = reinterpret_cast<Partial*>(wsb + off.parts);
-    if (!cached) {
-        // tables first, tile maps next, header (with the signature) last
-        WriteChunk c;
-        const size_t bytes_per = sizeof(c.data);
-        for (size_t pos = off.desc; pos < blob.size(); pos += bytes_per) {
-            const size_t len = (blob.size() - pos) < bytes_per ? (blob.size() - pos) : bytes_per;
-            c.offset = pos;
-            c.words = static_cast<uint32_t>(len / 4);
-            c.pad = 0;
-            std::memcpy(c.data, blob.data() + pos, len);
-            if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
-        }
-        if (launch_plan_tiles(desc_dev, T, map0, map1, stream) != hipSuccess) return ZERO_ERR_HIP;
-        c.offset = 0;
-        c.words = static_cast<uint32_t>(off.desc / 4);
-        c.pad = 0;
-        std::memcpy(c.data, blob.data(), off.desc);
-        if (launch_plan_write(wsb, c, stream) != hipSuccess) return ZERO_ERR_HIP;
-        std::lock_guard<std::mutex> lk(g_plan_mu);
-        g_plan_cache[key] = sig;
-    }
-
-    // ---- the step
-    const AdamScalars c = derive(hp);
-    const float gscale = static_cast<float>(hp->grad_scale);
-    const Mode first_mode = two_pass ? Mode::PassA : Mode::Full;
-    FinalizeArgs fin{res_dev, reinterpret_cast<unsigned*>(wsb + kCounterOffset), external_sumsq,
-                     hp->max_grad_norm, skip, ls, {}};
-    if (amp) fin.lscfg = *lscfg;
-    hipError_t e = launch_fused(first_mode, geom[0], hdr_dev, desc_dev, map0, tiles[0], sig, M, gscale, c, parts, fin,
-                                nullptr, stream);
-    if (e != hipSuccess) return ZERO_ERR_HIP;
-    if (two_pass) {
-        e = launch_fused(Mode::PassB, geom[1], hdr_dev, desc_dev, map1, tiles[1], sig, M, gscale, c, parts, fin,
-                         res_dev, stream);
-        if (e != hipSuccess) return ZERO_ERR_HIP;
-    }
-    return ZERO_OK;
+    return plan_offsets(sizes_of(tensors, T), M, two_pass_of(hp) ? PlanKind::StepTwoPass : PlanKind::Step).total;
 }
 
 int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
@@ -449,7 +527,7 @@ size_t zero_step_amp_workspace_bytes(const zero_tensor* tensors, int32_t T, int3
     if (T > 0 && tensors == nullptr) return 0;
     for (int32_t t = 0; t < T; ++t)
         if (tensors[t].n < 0) return 0;
-    return plan_offsets(tensors, T, M, true).total;
+    return plan_offsets(sizes_of(tensors, T), M, PlanKind::StepTwoPass).total;
 }
 
 int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
@@ -458,6 +536,111 @@ int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_a
 {
     if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     return step_impl(tensors, T, M, hp, external_sumsq, ws, ws_bytes, res_dev, stream, cfg, ls_dev);
+}
+
+// ------------------------------------------------------------------ ZeRO-2 streaming
+
+size_t zero_bucket_reduce_workspace_bytes(const zero_grad_shard* shards, int32_t T, int32_t M)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS) return 0;
+    if (T > 0 && shards == nullptr) return 0;
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) {
+        if (shards[t].n < 0) return 0;
+        ns.push_back(shards[t].n);
+    }
+    return plan_offsets(ns, M, PlanKind::Bucket).total;
+}
+
+int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                       uint64_t stamp, zero_bucket_partial* partial_dev, void* ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS) return ZERO_ERR_INVALID_ARGUMENT;
+    if ((flags & ~(ZERO_BUCKET_ACCUMULATE | ZERO_BUCKET_FINAL)) != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    const bool final = (flags & ZERO_BUCKET_FINAL) != 0;
+    if (final && (partial_dev == nullptr || !is_fin(grad_scale) || !(grad_scale > 0.0)))
+        return ZERO_ERR_INVALID_ARGUMENT;
+    if (T > 0 && shards == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    int64_t total_n = 0;
+    std::vector<PlanTensor> pts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_grad_shard& x = shards[t];
+        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.grad_acc) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t].grads = x.grads;
+        pts[t].acc = x.grad_acc;
+        total_n += x.n;
+    }
+    const float gscale = final ? static_cast<float>(grad_scale) : 1.0f;
+    if (total_n == 0)
+        return final ? hip_status(launch_bucket_partial_empty(partial_dev, stamp, gscale, stream)) : ZERO_OK;
+    Plan plan;
+    const int st = make_plan(pts, M, PlanKind::Bucket, ws, ws_bytes, stream, &plan);
+    if (st != ZERO_OK) return st;
+    FinalizeArgs fin{};
+    fin.counter = plan.counter;
+    fin.slot = partial_dev;
+    fin.stamp = stamp;
+    fin.accumulate = (flags & ZERO_BUCKET_ACCUMULATE) != 0;
+    fin.final = final;
+    return hip_status(launch_fused(Mode::Acc, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig,
+                                   M, gscale, AdamScalars{}, plan.parts, fin, nullptr, stream));
+}
+
+static bool acc_tensors_ok(const zero_acc_tensor* tensors, int32_t T)
+{
+    if (T < 0 || (T > 0 && tensors == nullptr)) return false;
+    for (int32_t t = 0; t < T; ++t)
+        if (tensors[t].n < 0) return false;
+    return true;
+}
+
+size_t zero_step_accumulated_workspace_bytes(const zero_acc_tensor* tensors, int32_t T)
+{
+    if (!acc_tensors_ok(tensors, T)) return 0;
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
+    return plan_offsets(ns, 0, PlanKind::AccStep).total;
+}
+
+int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                          const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                          double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
+                          hipStream_t stream)
+{
+    if (!acc_tensors_ok(tensors, T) || !hparams_ok(hp) || res_dev == nullptr || nbuckets < 0)
+        return ZERO_ERR_INVALID_ARGUMENT;
+    if (nbuckets > 0 && partials_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    int64_t total_n = 0;
+    std::vector<PlanTensor> pts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_acc_tensor& x = tensors[t];
+        pts[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grad_acc || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t] = PlanTensor{x.n, nullptr, x.master, x.exp_avg, x.exp_avg_sq, x.param_out, const_cast<float*>(x.grad_acc)};
+        total_n += x.n;
+    }
+    const float gscale = static_cast<float>(hp->grad_scale);
+    const int skip = hp->skip_on_nonfinite != 0;
+    if (total_n == 0)
+        return hip_status(launch_bucket_finalize(nullptr, 0, partials_dev, nbuckets, stamp, gscale, external_sumsq,
+                                                 hp->max_grad_norm, skip, res_dev, stream));
+    Plan plan;
+    const int st = make_plan(pts, 0, PlanKind::AccStep, ws, ws_bytes, stream, &plan);
+    if (st != ZERO_OK) return st;
+    hipError_t e = launch_bucket_finalize(plan.hdr, plan.sig, partials_dev, nbuckets, stamp, gscale, external_sumsq,
+                                          hp->max_grad_norm, skip, res_dev, stream);
+    if (e != hipSuccess) return ZERO_ERR_HIP;
+    FinalizeArgs fin{};
+    e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, 0, gscale,
+                     derive(hp), nullptr, fin, res_dev, stream);
+    return hip_status(e);
 }
 
 int zero_workspace_forget(const void* ws)

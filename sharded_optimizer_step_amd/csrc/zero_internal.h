@@ -102,8 +102,12 @@ struct alignas(16) PlanHeader {
     int32_t M;
     int32_t geom[2];   // kGeoms index of each pass
     int32_t two_pass;
-    int32_t pad;
+    int32_t kind;      // PlanKind
 };
+
+// What a workspace plan drives: the fused step (one or two passes), the
+// accumulation of one gradient bucket, or the step from accumulated gradients.
+enum class PlanKind : int32_t { Step = 0, StepTwoPass = 1, Bucket = 2, AccStep = 3 };
 
 // Byte offset, in the 256-byte header region of a zero_step workspace, of the
 // arrival counter of the fold pass (zero between launches).
@@ -119,6 +123,12 @@ struct FinalizeArgs {
     int skip;
     zero_loss_scale* ls;           // null unless AMP; the fold also reads its inv_scale
     zero_loss_scale_config lscfg;  // meaningful when ls is non-null
+    // bucket accumulation (Mode::Acc): the last workgroup of a final pass
+    // writes the bucket partial instead of a result record
+    zero_bucket_partial* slot;
+    uint64_t stamp;
+    int accumulate;                // add the fold to the accumulator
+    int final;                     // last micro-batch: norm partials into *slot
 };
 
 // Byte offsets of the regions of a zero_step workspace.
@@ -143,7 +153,8 @@ struct RankPtrs {
 enum class Mode : int {
     Full = 0,   // fold + unscale + check + AdamW + emit, one pass
     PassA = 1,  // fold + unscale + check, store fp32 g
-    PassB = 2,  // read fp32 g, AdamW + emit (coefficient/skip from the result record)
+    PassB = 2,  // read fp32 g, times gscale, AdamW + emit (coefficient/skip from the result record)
+    Acc = 3,    // fold into the fp32 accumulator; on the final pass, check + norm partials
 };
 
 // ---- launch wrappers (zero_kernels.hip); all return a hipError_t ----------
@@ -157,6 +168,14 @@ hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint1
 // in index order into the result record.
 hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external, double max_norm, int skip,
                            zero_result* res, hipStream_t s);
+// The bucket partials of a ZeRO-2 step combined in index order into the
+// result record, each checked against the step's stamp and fp32 scale; a
+// stale plan `hdr` (may be null) is reported instead.
+hipError_t launch_bucket_finalize(const PlanHeader* hdr, uint64_t sig, const zero_bucket_partial* parts, int32_t nb,
+                                  uint64_t stamp, float scale, double external, double max_norm, int skip,
+                                  zero_result* res, hipStream_t s);
+// The partial of a final bucket pass over no elements.
+hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale, hipStream_t s);
 hipError_t launch_loss_scale_init(const zero_loss_scale& s, zero_loss_scale* ls, hipStream_t st);
 hipError_t launch_loss_scale_update(const zero_loss_scale_config& c, const zero_result* res, zero_loss_scale* ls,
                                     hipStream_t st);

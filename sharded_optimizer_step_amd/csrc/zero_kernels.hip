@@ -243,7 +243,7 @@ __device__ __forceinline__ void combine_published(Partial* parts, int64_t n, dou
 
 // ------------------------------------------------------------------ tile body
 
-enum class Op : int { Reduce, Check, Adam, Full, PassA };
+enum class Op : int { Reduce, Check, Adam, Full, PassA, Acc };
 
 // Pointers and layout of one shard, as seen by one tile.
 struct Ctx {
@@ -253,16 +253,18 @@ struct Ctx {
     float* m;
     float* v;
     uint16_t* out;
-    float* gout;        // fp32 gradient written (Reduce, PassA)
-    const float* gin;   // fp32 gradient read (Check, Adam; Reduce continuing a fold)
+    float* gout;        // fp32 gradient written (Reduce, PassA, Acc)
+    const float* gin;   // fp32 gradient read (Check, Adam, Acc; Reduce continuing a fold)
     int64_t n, nvec;
     int32_t head, tail;
 };
 
 struct Scal {
-    float gscale;  // multiplier of the fp32 sum (applied when `last`)
-    double coef;   // clip coefficient (Adam, Full)
-    bool last;     // Reduce: this pass ends the fold
+    float gscale;     // multiplier of the fp32 sum (Reduce: applied when `last`); Adam: of the stored g
+    double coef;      // clip coefficient (Adam, Full)
+    bool last;        // Reduce: this pass ends the fold
+    bool accumulate;  // Acc: add the fold to the accumulator (else store it)
+    bool final;       // Acc: also check and square g = acc * gscale
 };
 
 // One element, scalar path.
@@ -277,8 +279,21 @@ __device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamSc
         x.gout[e] = g;
         return;
     }
+    if constexpr (OP == Op::Acc) {
+        float a = fold_one<MT, true>(x.gp, x.M, e, 0.0f);
+        if (k.accumulate) a = x.gin[e] + a;
+        x.gout[e] = a;
+        if (k.final) {
+            g = a * k.gscale;
+            bad |= nonfinite(g);
+            const double d = static_cast<double>(g);
+            acc = fma(d, d, acc);
+        }
+        return;
+    }
     if constexpr (OP == Op::Full || OP == Op::PassA) g = fold_one<MT, true>(x.gp, x.M, e, 0.0f) * k.gscale;
-    if constexpr (OP == Op::Check || OP == Op::Adam) g = x.gin[e];
+    if constexpr (OP == Op::Check) g = x.gin[e];
+    if constexpr (OP == Op::Adam) g = x.gin[e] * k.gscale;
     if constexpr (OP != Op::Adam) {
         bad |= nonfinite(g);
         const double d = static_cast<double>(g);
@@ -350,6 +365,10 @@ __device__ __forceinline__ void do_vec(const Ctx& x, const Scal& k, const AdamSc
         const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
         g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w; g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
     }
+    if constexpr (OP == Op::Adam) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[j] = g[j] * k.gscale;
+    }
     if constexpr (OP != Op::Adam) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -407,7 +426,7 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
     }
     const int lane = tid & 63, wave = tid >> 6;
     const int64_t v0 = t * kTileVecs + static_cast<int64_t>(wave) * 64 * U + lane;
-    if constexpr (OP == Op::Full || OP == Op::PassA) {
+    if constexpr (OP == Op::Full || OP == Op::PassA || OP == Op::Acc) {
         bool ok[U];
         float s[U][8];
         const uint16_t* p0 = rank_ptr(x.gp, 0) + x.head;
@@ -436,6 +455,30 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
         for (int u = 0; u < U; ++u) {
             if (!ok[u]) continue;
             const int64_t e0 = x.head + (v0 + u * 64) * kVec;
+            if constexpr (OP == Op::Acc) {
+                // the running sum of the reduce-scatter results: acc + fold
+                float a[8];
+                if (k.accumulate) {
+                    const f32x4 p = ld4(x.gin + e0), q = ld4(x.gin + e0 + 4);
+                    a[0] = p.x + s[u][0]; a[1] = p.y + s[u][1]; a[2] = p.z + s[u][2]; a[3] = p.w + s[u][3];
+                    a[4] = q.x + s[u][4]; a[5] = q.y + s[u][5]; a[6] = q.z + s[u][6]; a[7] = q.w + s[u][7];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a[j] = s[u][j];
+                }
+                st4(x.gout + e0, f32x4{a[0], a[1], a[2], a[3]});
+                st4(x.gout + e0 + 4, f32x4{a[4], a[5], a[6], a[7]});
+                if (k.final) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float g = a[j] * k.gscale;
+                        bad |= nonfinite(g);
+                        const double d = static_cast<double>(g);
+                        acc = fma(d, d, acc);
+                    }
+                }
+                continue;
+            }
             float g[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -459,7 +502,8 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
             if (v < x.nvec) {
                 const int64_t e0 = x.head + v * kVec;
                 const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
-                const float g[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                const float g[8] = {a.x * k.gscale, a.y * k.gscale, a.z * k.gscale, a.w * k.gscale,
+                                    b.x * k.gscale, b.y * k.gscale, b.z * k.gscale, b.w * k.gscale};
                 adam8(x, k, c, e0, g);
             }
         }
@@ -508,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(RankPtrs ptrs, int Mc,
     x.M = Mc;
     x.gout = g_out;
     x.gin = g_out;
-    const Scal k{scale, 1.0, last != 0};
+    const Scal k{scale, 1.0, last != 0, false, false};
     const AdamScalars c{};
     double acc = 0.0;
     uint32_t bad = 0;
@@ -521,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const float* __restrict
 {
     Ctx x = ctx_flat(L);
     x.gin = g;
-    const Scal k{1.0f, 1.0, false};
+    const Scal k{1.0f, 1.0, false, false, false};
     const AdamScalars c{};
     double acc = 0.0;
     uint32_t bad = 0;
@@ -546,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(float* __restrict__ mas
     x.v = v;
     x.out = out;
     x.gin = g;
-    const Scal k{1.0f, coef, false};
+    const Scal k{1.0f, coef, false, false, false};
     double acc = 0.0;
     uint32_t bad = 0;
     const int64_t tiles = layout_tiles(L);
@@ -575,7 +619,18 @@ __device__ __forceinline__ zero_result make_record(double sumsq, uint32_t bad, d
     return r;
 }
 
-__device__ __forceinline__ zero_result stale_record()
+__device__ __forceinline__ zero_bucket_partial bucket_partial(double sumsq, uint32_t bad, uint64_t stamp, float scale)
+{
+    zero_bucket_partial p;
+    p.sumsq = sumsq;
+    p.stamp = stamp;
+    p.found_inf = bad != 0 ? 1 : 0;
+    p.grad_scale = scale;
+    p.reserved = 0;
+    return p;
+}
+
+__device__ __forceinline__ zero_result error_record(int32_t status)
 {
     zero_result r;
     r.sumsq = __builtin_nan("");
@@ -583,9 +638,11 @@ __device__ __forceinline__ zero_result stale_record()
     r.grad_norm = __builtin_nanf("");
     r.found_inf = 0;
     r.skipped = 1;
-    r.status = ZERO_ERR_STALE_WORKSPACE;
+    r.status = status;
     return r;
 }
+
+__device__ __forceinline__ zero_result stale_record() { return error_record(ZERO_ERR_STALE_WORKSPACE); }
 
 // One move of the dynamic loss scale on a step's overflow flag (the rule is
 // stated with zero_loss_scale in zero_step.h: hysteresis-th overflow in a row
@@ -644,8 +701,12 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
                                                    const zero_result* __restrict__ res)
 {
     if (hdr->signature != sig) {  // the workspace no longer holds this plan: write nothing but the record
-        if constexpr (MODE != Mode::PassB) {
-            if (blockIdx.x == 0 && threadIdx.x == 0) *fin.res = stale_record();
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if constexpr (MODE == Mode::Acc) {
+                if (fin.slot != nullptr) *fin.slot = bucket_partial(0.0, 0, ~fin.stamp, gscale);
+            } else if constexpr (MODE != Mode::PassB) {
+                *fin.res = stale_record();
+            }
         }
         return;
     }
@@ -654,19 +715,25 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
         if (res->skipped != 0 || res->status != 0) return;
         coef = res->clip_coef;
     }
-    if constexpr (MODE != Mode::PassB) {
+    if constexpr (MODE == Mode::Full || MODE == Mode::PassA) {
         if (fin.ls != nullptr) gscale = gscale * fin.ls->inv_scale;  // AMP: the scale of this step
     }
-    constexpr Op OP = MODE == Mode::Full ? Op::Full : (MODE == Mode::PassA ? Op::PassA : Op::Adam);
-    const Scal k{gscale, coef, false};
+    constexpr Op OP = MODE == Mode::Full    ? Op::Full
+                      : MODE == Mode::PassA ? Op::PassA
+                      : MODE == Mode::Acc   ? Op::Acc
+                                            : Op::Adam;
+    const Scal k{gscale, coef, false, fin.accumulate != 0, fin.final != 0};
     double acc = 0.0;
     uint32_t bad = 0;
     const TileRef tr = map[blockIdx.x];
     const Ctx x = ctx_of(desc[tr.tensor], M);
     big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
+    if constexpr (MODE == Mode::Acc) {
+        if (!k.final) return;  // uniform over the launch
+    }
     if constexpr (MODE != Mode::PassB) {
-        // the last workgroup to arrive writes the record and re-arms the
-        // counter for the next launch
+        // the last workgroup to arrive writes the record (the bucket partial
+        // when accumulating) and re-arms the counter for the next launch
         block_reduce<NT>(acc, bad);
         __shared__ int s_last;
         if (threadIdx.x == 0) s_last = publish_and_arrive(parts + blockIdx.x, acc, bad, fin.counter) == gridDim.x - 1;
@@ -676,9 +743,13 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
             uint32_t nbad;
             combine_published<NT>(parts, gridDim.x, sumsq, nbad);
             if (threadIdx.x == 0) {
-                *fin.res = make_record(sumsq, nbad, fin.external, fin.max_norm, fin.skip);
-                // every other workgroup has arrived, so none still reads inv_scale
-                if (fin.ls != nullptr) loss_scale_move(fin.lscfg, nbad != 0, fin.ls);
+                if constexpr (MODE == Mode::Acc) {
+                    *fin.slot = bucket_partial(sumsq, nbad, fin.stamp, gscale);
+                } else {
+                    *fin.res = make_record(sumsq, nbad, fin.external, fin.max_norm, fin.skip);
+                    // every other workgroup has arrived, so none still reads inv_scale
+                    if (fin.ls != nullptr) loss_scale_move(fin.lscfg, nbad != 0, fin.ls);
+                }
                 __hip_atomic_store(fin.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -695,6 +766,40 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
     uint32_t bad;
     combine_partials<kThreads>(parts, nparts, sumsq, bad);
     if (threadIdx.x == 0) *res = make_record(sumsq, bad, external, max_norm, skip);
+}
+
+// One workgroup: the bucket partials of a ZeRO-2 step in index order (the
+// same fixed tree as combine_partials), each checked against the step's
+// stamp and fp32 scale, then the norm, clip coefficient and skip decision.
+// hdr (null when the step has no elements) is the plan of the update pass
+// that follows: a stale one is reported here, before that pass skips.
+__global__ __launch_bounds__(kThreads) void bucket_finalize_kernel(const PlanHeader* __restrict__ hdr, uint64_t sig,
+                                                                   const zero_bucket_partial* __restrict__ parts,
+                                                                   int32_t nb, uint64_t stamp, float scale,
+                                                                   double external, double max_norm, int skip,
+                                                                   zero_result* __restrict__ res)
+{
+    if (hdr != nullptr && hdr->signature != sig) {
+        if (threadIdx.x == 0) *res = stale_record();
+        return;
+    }
+    double sumsq = 0.0;
+    uint32_t flags = 0;  // bit 0: a non-finite gradient; bit 1: a partial of another step or scale
+    for (int32_t i = threadIdx.x; i < nb; i += kThreads) {
+        const zero_bucket_partial p = parts[i];
+        sumsq += p.sumsq;
+        flags |= p.found_inf != 0 ? 1u : 0u;
+        flags |= (p.stamp != stamp || __float_as_uint(p.grad_scale) != __float_as_uint(scale)) ? 2u : 0u;
+    }
+    block_reduce<kThreads>(sumsq, flags);
+    if (threadIdx.x == 0)
+        *res = (flags & 2u) ? error_record(ZERO_ERR_BUCKET_PARTIALS)
+                            : make_record(sumsq, flags & 1u, external, max_norm, skip);
+}
+
+__global__ void bucket_partial_empty_kernel(zero_bucket_partial* __restrict__ slot, uint64_t stamp, float scale)
+{
+    if (threadIdx.x == 0) *slot = bucket_partial(0.0, 0, stamp, scale);
 }
 
 __global__ void loss_scale_init_kernel(zero_loss_scale s, zero_loss_scale* __restrict__ ls)
@@ -842,6 +947,20 @@ hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external
     return hipGetLastError();
 }
 
+hipError_t launch_bucket_finalize(const PlanHeader* hdr, uint64_t sig, const zero_bucket_partial* parts, int32_t nb,
+                                  uint64_t stamp, float scale, double external, double max_norm, int skip,
+                                  zero_result* res, hipStream_t s)
+{
+    bucket_finalize_kernel<<<1, kThreads, 0, s>>>(hdr, sig, parts, nb, stamp, scale, external, max_norm, skip, res);
+    return hipGetLastError();
+}
+
+hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale, hipStream_t s)
+{
+    bucket_partial_empty_kernel<<<1, 64, 0, s>>>(slot, stamp, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_loss_scale_init(const zero_loss_scale& s, zero_loss_scale* ls, hipStream_t st)
 {
     loss_scale_init_kernel<<<1, 64, 0, st>>>(s, ls);
@@ -879,6 +998,8 @@ hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const Tensor
         return fused_dispatch<Mode::PassA>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
     case Mode::PassB:
         return fused_dispatch<Mode::PassB>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
+    case Mode::Acc:
+        return fused_dispatch<Mode::Acc>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
     }
     return hipErrorInvalidValue;
 }

@@ -117,4 +117,36 @@ def workload(i: int) -> Workload:
     raise ValueError(i)
 
 
+# Gradient buckets of the ZeRO-2 streaming step (gsyq.cn/news/457874 section
+# 4.2: reduce_bucket_size 5e7 elements). Backward produces a layer's
+# gradients in the reverse of the order the forward pass uses its tensors,
+# from the last layer to the first.
+REDUCE_BUCKET_ELEMS = 50_000_000
+_LLAMA_FORWARD = ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")
+
+
+def backward_order(w: Workload) -> List[int]:
+    """Tensor indices of w in the order backward produces their gradients."""
+    if len(w.tensors) == 1:
+        return [0]
+    by_name = {t.name: i for i, t in enumerate(w.tensors)}
+    layers = sorted({int(t.name.split(".")[1]) for t in w.tensors}, reverse=True)
+    return [by_name[f"layers.{L}.{nm}"] for L in layers for nm in reversed(_LLAMA_FORWARD)]
+
+
+def zero2_buckets(w: Workload, bucket_elems: int = REDUCE_BUCKET_ELEMS) -> List[List[int]]:
+    """Tensor indices grouped into buckets in backward order; a bucket closes
+    once the whole (unsharded) tensors in it reach bucket_elems elements."""
+    out, cur, size = [], [], 0
+    for i in backward_order(w):
+        cur.append(i)
+        size += w.tensors[i].full
+        if size >= bucket_elems:
+            out.append(cur)
+            cur, size = [], 0
+    if cur:
+        out.append(cur)
+    return out
+
+
 WORKLOADS = [workload(i) for i in range(5)]

@@ -48,7 +48,8 @@ def test_struct_layouts_match_header(tmp_path):
     ctypes mirrors of the Python binding."""
     import subprocess
     fields = {"zero_adamw_hparams": z._CHparams, "zero_tensor": z._CTensor,
-              "zero_loss_scale_config": z._CLossScaleConfig}
+              "zero_loss_scale_config": z._CLossScaleConfig, "zero_grad_shard": z._CGradShard,
+              "zero_acc_tensor": z._CAccTensor}
     body = []
     for cname, cls in fields.items():
         body.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -58,6 +59,9 @@ def test_struct_layouts_match_header(tmp_path):
     body.append('printf("zero_loss_scale %zu\\n", sizeof(zero_loss_scale));')
     for f in ("scale", "inv_scale", "good_steps", "overflows"):
         body.append(f'printf("zero_loss_scale.{f} %zu\\n", offsetof(zero_loss_scale, {f}));')
+    body.append('printf("zero_bucket_partial %zu\\n", sizeof(zero_bucket_partial));')
+    for f in ("sumsq", "stamp", "found_inf", "grad_scale", "reserved"):
+        body.append(f'printf("zero_bucket_partial.{f} %zu\\n", offsetof(zero_bucket_partial, {f}));')
     src = tmp_path / "layout.c"
     src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"zero_step.h\"\nint main(void){" +
                    "".join(body) + "return 0;}\n")
@@ -74,6 +78,10 @@ def test_struct_layouts_match_header(tmp_path):
     # read_loss_scale unpacks "<ffii"
     assert int(got["zero_loss_scale"]) == z.LOSS_SCALE_BYTES
     assert [int(got[f"zero_loss_scale.{f}"]) for f in ("scale", "inv_scale", "good_steps", "overflows")] == [0, 4, 8, 12]
+    # read_bucket_partial unpacks "<dQifq"
+    assert int(got["zero_bucket_partial"]) == z.BUCKET_PARTIAL_BYTES
+    assert [int(got[f"zero_bucket_partial.{f}"]) for f in ("sumsq", "stamp", "found_inf", "grad_scale",
+                                                           "reserved")] == [0, 8, 16, 20, 24]
 
 
 def test_status_strings():
@@ -214,3 +222,66 @@ def test_loss_scale_entry_points_need_their_buffers():
                            None) == 1
     assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), ctypes.byref(c), ctypes.c_void_p(1 << 20), 0.0, 1 << 24,
                            need - 1, res, None) == 2
+
+
+def _shards(n=100, M=2, acc=4096):
+    ptrs = (ctypes.c_void_p * M)(*[256 * (r + 1) for r in range(M)])
+    arr = (z._CGradShard * 1)()
+    arr[0] = z._CGradShard(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), acc)
+    return arr, ptrs
+
+
+def test_bucket_reduce_argument_checks():
+    L = z.lib()
+    arr, keep = _shards()
+    need = L.zero_bucket_reduce_workspace_bytes(arr, 1, 2)
+    assert need > 0
+    part, ws = ctypes.c_void_p(1 << 20), 1 << 24
+    A, F = z.BUCKET_ACCUMULATE, z.BUCKET_FINAL
+    assert L.zero_bucket_reduce(arr, 1, 2, 4, 1.0, 0, part, ws, need, None) == 1           # unknown flag
+    assert L.zero_bucket_reduce(arr, 1, 2, F, 1.0, 0, None, ws, need, None) == 1           # final, no partial
+    assert L.zero_bucket_reduce(arr, 1, 2, F | A, 0.0, 0, part, ws, need, None) == 1       # final, scale <= 0
+    assert L.zero_bucket_reduce(arr, 1, 2, F, float("inf"), 0, part, ws, need, None) == 1
+    assert L.zero_bucket_reduce(arr, 1, 0, A, 1.0, 0, part, ws, need, None) == 1            # M < 1
+    assert L.zero_bucket_reduce(arr, -1, 2, A, 1.0, 0, part, ws, need, None) == 1
+    assert L.zero_bucket_reduce(None, 1, 2, A, 1.0, 0, part, ws, need, None) == 1
+    assert L.zero_bucket_reduce(arr, 1, 2, A, 1.0, 0, part, ws, need - 1, None) == 2        # ws short
+    assert L.zero_bucket_reduce(arr, 1, 2, A, 1.0, 0, part, ws + 16, need, None) == 1       # ws misaligned
+    assert L.zero_bucket_reduce(arr, 1, 2, A, 1.0, 0, part, None, need, None) == 1          # no ws
+    nacc, k2 = _shards(acc=0)
+    assert L.zero_bucket_reduce(nacc, 1, 2, A, 1.0, 0, part, ws, need, None) == 1           # no accumulator
+    nul = (ctypes.c_void_p * 2)(256, None)
+    arr2 = (z._CGradShard * 1)()
+    arr2[0] = z._CGradShard(100, ctypes.cast(nul, ctypes.POINTER(ctypes.c_void_p)), 4096)
+    assert L.zero_bucket_reduce(arr2, 1, 2, A, 1.0, 0, part, ws, need, None) == 1           # a null replica
+    assert L.zero_bucket_reduce(arr, 0, 2, A, 1.0, 0, None, None, 0, None) == 0             # empty, not final
+    neg, k3 = _shards(n=-1)
+    assert L.zero_bucket_reduce_workspace_bytes(neg, 1, 2) == 0
+    assert L.zero_bucket_reduce_workspace_bytes(arr, 1, 0) == 0
+
+
+def test_step_accumulated_argument_checks():
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    arr = (z._CAccTensor * 1)()
+    big = (z._CAccTensor * 1)()
+    big[0] = z._CAccTensor(1_000_000, 256, 1024, 2048, 4096, 8192)
+    # no gradient copy: the step reads the caller's accumulator
+    assert 0 < L.zero_step_accumulated_workspace_bytes(big, 1) < 1_000_000 // 100
+    arr[0] = z._CAccTensor(100, 256, 1024, 2048, 4096, 8192)
+    need = L.zero_step_accumulated_workspace_bytes(arr, 1)
+    parts, res, ws = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 1 << 24
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(h), parts, 1, 0, 0.0, ws, need, None, None) == 1  # no res
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(h), None, 1, 0, 0.0, ws, need, res, None) == 1   # no partials
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(h), parts, -1, 0, 0.0, ws, need, res, None) == 1
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(h), parts, 1, 0, 0.0, ws, need - 1, res, None) == 2
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(h), parts, 1, 0, 0.0, None, need, res, None) == 1
+    bad = _hp(step=0)
+    assert L.zero_step_accumulated(arr, 1, ctypes.byref(bad), parts, 1, 0, 0.0, ws, need, res, None) == 1
+    arr2 = (z._CAccTensor * 1)()
+    arr2[0] = z._CAccTensor(100, None, 1024, 2048, 4096, 8192)
+    assert L.zero_step_accumulated(arr2, 1, ctypes.byref(h), parts, 1, 0, 0.0, ws, need, res, None) == 1
+    arr3 = (z._CAccTensor * 1)()
+    arr3[0] = z._CAccTensor(-1, None, None, None, None, None)
+    assert L.zero_step_accumulated_workspace_bytes(arr3, 1) == 0
+    assert L.zero_step_accumulated(arr3, 1, ctypes.byref(h), parts, 1, 0, 0.0, ws, need, res, None) == 1
