@@ -204,8 +204,13 @@ def zero2_line(a, w, tensors) -> dict:
     bpp = b_reduce + b_update
     dom = ("update", b_update, update_ms) if update_ms >= reduce_ms else ("bucket reduces", b_reduce, reduce_ms)
     achieved = dom[1] * n / (dom[2] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and K == 1:
+        ent = json.load(open(TRAFFIC_FILE)).get(f"{w.index}_zero2_K1")
+        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and ent.get("kernel") == dom[0]:
+            traffic = ent["bytes_per_launch"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     cfg = {"workload": w.name + f", ZeRO-2 streaming: {len(buckets)} buckets of reduce_bucket_size 5e7 "
                                 f"in backward order, {K} micro-batch(es)",
            "shard_params": n, "M": w.M, "tensors": len(w.tensors), "buckets": len(buckets), "micro_batches": K,

@@ -3,6 +3,7 @@ HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter passes (one
 counter per run), calibrated on a plain device copy of known size.
 
     python bench_profile.py --workload 2 [--steps 10] [--out gpurun_out/prof]
+    python bench_profile.py --zero2 [--workload 3]     (the ZeRO-2 streaming leg of bench.py)
 
 Runs on a GPU machine. Writes:
   profiles/<kernel>_<workload tag>.md   the figures used and the commands that made them
@@ -62,7 +63,10 @@ def main():
     ap.add_argument("--out", default=os.path.join("gpurun_out", "prof"), help="raw rocprofv3 output (relative)")
     ap.add_argument("--profiles-dir", default="profiles", help="where the summaries go (relative)")
     ap.add_argument("--summarize-only", action="store_true", help="re-read existing raw output, run nothing")
+    ap.add_argument("--zero2", action="store_true", help="profile bench.py --zero2 (one micro-batch)")
     a = ap.parse_args()
+    if a.zero2:
+        return main_zero2(a)
     sys.path.insert(0, ROOT)
     from synth.workloads import workload
     w = workload(a.workload)
@@ -147,6 +151,101 @@ def main():
                            "write_bytes": round(write_b), "algorithmic_bytes": alg,
                            "rocprof_avg_us": round(avg_us, 2), "fetch_factor": round(f_fetch, 5),
                            "write_factor": round(f_write, 5), "summary": os.path.join("profiles", os.path.basename(md))}
+    json.dump(tf, open(tf_path, "w"), indent=1, sort_keys=True)
+    print(open(md).read())
+
+
+def main_zero2(a):
+    """The ZeRO-2 leg: every bucket reduce (Mode::Acc launches, one per bucket
+    and step) and the update (one Mode::PassB launch per step), aggregated per
+    step; the dominant phase gets the counter-measured traffic."""
+    sys.path.insert(0, ROOT)
+    from synth.workloads import workload, zero2_buckets
+    wi = 3 if a.workload == 2 else a.workload
+    w = workload(wi)
+    nb = len(zero2_buckets(w))
+    out = os.path.join(a.out, f"w{wi}_zero2")
+    os.chdir(ROOT)
+    os.makedirs(out, exist_ok=True)
+    warm = 2
+    bench = ["python", "-u", "bench.py", "--zero2", "--workload", str(wi), "--cpu-sample", "0", "--steps",
+             str(a.steps), "--warmup", str(warm)]
+    calib = ["python", "-u", "bench.py", "--calib-copy", "--steps", "3"]
+    rp = "rocprofv3"
+    cmds = {
+        "trace": [rp, "--kernel-trace", "--stats", "--output-format", "csv", "-d", f"{out}/trace", "-o", "run",
+                  "--"] + bench,
+        "fetch": [rp, "--pmc", "FETCH_SIZE", "--output-format", "csv", "-d", f"{out}/fetch", "-o", "run", "--"] + bench,
+        "write": [rp, "--pmc", "WRITE_SIZE", "--output-format", "csv", "-d", f"{out}/write", "-o", "run", "--"] + bench,
+        "cfetch": [rp, "--pmc", "FETCH_SIZE", "--output-format", "csv", "-d", f"{out}/cfetch", "-o", "run", "--"] + calib,
+        "cwrite": [rp, "--pmc", "WRITE_SIZE", "--output-format", "csv", "-d", f"{out}/cwrite", "-o", "run", "--"] + calib,
+    }
+    if not a.summarize_only:
+        for k, c in cmds.items():
+            run(c, f"{out}/{k}.log")
+    steps = a.steps + warm
+    stats = list(csv.DictReader(open(one(f"{out}/trace/run_kernel_stats.csv"))))
+    groups = {"bucket reduces": "(zero::Mode)3", "update": "(zero::Mode)2"}
+    n = w.n_total
+    alg = {"bucket reduces": (2 * w.M + 4) * n, "update": 30 * n}
+    per = {}
+    for g, tag in groups.items():
+        rows = [r for r in stats if "fused_kernel" in r["Name"] and tag in r["Name"]]
+        per[g] = dict(rows=rows, ns=sum(float(r["TotalDurationNs"]) for r in rows) / steps,
+                      calls=sum(int(r["Calls"]) for r in rows) / steps)
+    dom = max(per, key=lambda g: per[g]["ns"])
+    pred = lambda name, tag=groups[dom]: "fused_kernel" in name and tag in name
+    copy_name = "__amd_rocclr_copyBuffer"
+
+    def counter_total(path, kernel_pred):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kernel_pred(r["Kernel_Name"])]
+        if not vals:
+            sys.exit(f"no matching dispatch in {path}")
+        return sum(vals), len(vals)
+
+    fetch_kib, nf = counter_total(one(f"{out}/fetch/run_counter_collection.csv"), pred)
+    write_kib, nw = counter_total(one(f"{out}/write/run_counter_collection.csv"), pred)
+    cf_kib, _ = counter_per_dispatch(one(f"{out}/cfetch/run_counter_collection.csv"), lambda nm: nm == copy_name)
+    cw_kib, _ = counter_per_dispatch(one(f"{out}/cwrite/run_counter_collection.csv"), lambda nm: nm == copy_name)
+    copy_bytes = 4 << 30
+    f_fetch = cf_kib * 1024 / copy_bytes
+    f_write = cw_kib * 1024 / copy_bytes
+    fetch_b = fetch_kib * 1024 / f_fetch / steps
+    write_b = write_kib * 1024 / f_write / steps
+    os.makedirs(a.profiles_dir, exist_ok=True)
+    md = os.path.join(a.profiles_dir, f"zero2_bucket_reduce_and_update_{TAGS[wi]}.md")
+    with open(md, "w") as f:
+        f.write(f"# ZeRO-2 streaming step on {w.name}: {nb} bucket reduces + one update per step\n\n")
+        f.write("Commands (repository root, MI355X, ROCm 7.2):\n\n")
+        for k, c in cmds.items():
+            f.write(f"    {' '.join(c)}\n")
+        f.write(f"\nKernel stats (rocprofv3 --kernel-trace --stats) over {steps} steps ({warm} warm-up):\n\n")
+        f.write("| kernel | calls | average us | min us | max us | total us |\n|---|---|---|---|---|---|\n")
+        for g in groups:
+            for r in per[g]["rows"]:
+                nm = r["Name"].replace("void zero::(anonymous namespace)::", "")
+                nm = re.split(r"\((?:zero::PlanHeader|zero::Partial)", nm)[0]
+                f.write(f"| {nm} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {float(r['MinNs'])/1e3:.2f} | "
+                        f"{float(r['MaxNs'])/1e3:.2f} | {float(r['TotalDurationNs'])/1e3:.1f} |\n")
+        f.write("\nPer step:\n\n| phase | launches | kernel time us | algorithmic bytes | GB/s |\n|---|---|---|---|---|\n")
+        for g in groups:
+            f.write(f"| {g} | {per[g]['calls']:.0f} | {per[g]['ns'] / 1e3:.1f} | {alg[g]:,} | "
+                    f"{alg[g] / per[g]['ns']:.1f} |\n")
+        f.write(f"\nDominant phase: {dom} ({alg[dom] / n:.0f} B per parameter x {n:,} parameters).\n\n")
+        f.write("HBM counters of the dominant phase per step, calibrated on a 4 GiB device copy:\n\n")
+        f.write(f"- copy calibration: factors {f_fetch:.4f} (FETCH_SIZE), {f_write:.4f} (WRITE_SIZE)\n")
+        f.write(f"- FETCH_SIZE over {nf} dispatches -> {fetch_b:,.0f} B read per step\n")
+        f.write(f"- WRITE_SIZE over {nw} dispatches -> {write_b:,.0f} B written per step\n")
+        f.write(f"- traffic {fetch_b + write_b:,.0f} B per step = {(fetch_b + write_b) / alg[dom]:.4f} x the "
+                f"algorithmic bytes\n")
+        f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
+    tf_path = os.path.join(a.profiles_dir, "traffic.json")
+    tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
+    tf[f"{wi}_zero2_K1"] = {"kernel": dom, "kernel_source_sha256_16": src_hash(),
+                            "bytes_per_launch": round(fetch_b + write_b), "read_bytes": round(fetch_b),
+                            "write_bytes": round(write_b), "algorithmic_bytes": alg[dom],
+                            "rocprof_us_per_step": round(per[dom]["ns"] / 1e3, 2), "fetch_factor": round(f_fetch, 5),
+                            "write_factor": round(f_write, 5), "summary": os.path.join("profiles", os.path.basename(md))}
     json.dump(tf, open(tf_path, "w"), indent=1, sort_keys=True)
     print(open(md).read())
 
