@@ -20,6 +20,10 @@ ragged Llama-7B-shaped bucket list): each step reduces every gradient bucket
 (reduce_bucket_size 5e7 elements, backward order) into the fp32 shard
 accumulators with zero_bucket_reduce, for --micro-batches micro-batches,
 then applies zero_step_accumulated.
+
+--offload times the CPU-offloaded form (default workload: the 7.5B shard):
+the fold and norm on the GPU, the fp32 gradient to pinned host memory, AdamW
+on host threads over host-resident state, the bf16 shard back to the device.
 """
 from __future__ import annotations
 
@@ -59,6 +63,9 @@ def parse():
     p.add_argument("--zero2", action="store_true",
                    help="the ZeRO-2 streaming step: per-bucket zero_bucket_reduce, then zero_step_accumulated")
     p.add_argument("--micro-batches", type=int, default=1, help="--zero2: micro-batches accumulated per step")
+    p.add_argument("--offload", action="store_true",
+                   help="the CPU-offloaded step: zero_offload_step with the optimizer state in host memory")
+    p.add_argument("--threads", type=int, default=0, help="--offload: host threads (0: the CPU affinity mask)")
     p.add_argument("--amp", action="store_true",
                    help="step with zero_step_amp: the loss scale held on the device, starting at the workload's "
                         "1/grad_scale (a power of two), window 1000, hysteresis 2")
@@ -223,6 +230,77 @@ def zero2_line(a, w, tensors) -> dict:
     return {"value": n / (avg_ms * 1e-3), "ms_per_step": avg_ms, "config": cfg, "roofline": roofline}
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction: the MI355X host link (public specification)
+
+
+def offload_line(a, w, tensors) -> dict:
+    """Times the CPU-offloaded step; returns the fields of the JSON line. The
+    step is synchronous (it returns once the host state is updated), so it is
+    timed on the host clock between device synchronizations."""
+    import torch
+
+    import sharded_optimizer_step_amd as z
+
+    ots = [z.OffloadTensor(t.grads, t.master.cpu(), t.exp_avg.cpu(), t.exp_avg_sq.cpu(), t.param_out)
+           for t in tensors]
+    for t in tensors:  # the optimizer state now lives in host memory only
+        t.master = t.exp_avg = t.exp_avg_sq = None
+    torch.cuda.empty_cache()
+    ws = z.workspace(z.zero_offload_workspace_bytes(ots, w.M))
+    hws = z.host_workspace(z.zero_offload_host_workspace_bytes(ots))
+    hp0 = w.hparams()
+    hp = z.HParams(**hp0)
+    stream = torch.cuda.current_stream()
+    threads = a.threads
+    for i in range(a.warmup):
+        hp.step = hp0["step"] + i
+        r = z.zero_offload_step(ots, hp, 0.0, ws, hws, threads, stream)
+    torch.cuda.synchronize()
+    if r["status"] != 0:
+        raise RuntimeError(f"step status {r}")
+    S = a.steps
+    per = []
+    torch.cuda.synchronize()
+    t_all = time.perf_counter()
+    for i in range(S):
+        hp.step = hp0["step"] + a.warmup + i
+        t0 = time.perf_counter()
+        z.zero_offload_step(ots, hp, 0.0, ws, hws, threads, stream)
+        per.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t_all
+    n = w.n_total
+    # the two limits of the offloaded step, each timed alone
+    g_dev = torch.empty(n, dtype=torch.float32, device="cuda")
+    g_host = torch.empty(n, dtype=torch.float32, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        g_host.copy_(g_dev, non_blocking=True)
+    torch.cuda.synchronize()
+    d2h_gbs = 3 * 4 * n / (time.perf_counter() - t0) / 1e9
+    h = ots[0]
+    k = h.master.numel()
+    out_h = torch.zeros(k, dtype=torch.bfloat16, pin_memory=True)
+    g_host[:k].zero_()
+    host_s = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        z.zero_offload_adamw_host(h.master, h.exp_avg, h.exp_avg_sq, g_host[:k], out_h, hp, 1.0, threads)
+        host_s.append(time.perf_counter() - t0)
+    host_pps = k / min(host_s)
+    step_s = total_s / S
+    link = 6 * n / step_s / 1e9  # 4 B of gradient down, 2 B of bf16 up per parameter
+    roofline = {"bound": "pcie", "achieved": round(4 * n / step_s / 1e9, 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                "frac": round(4 * n / step_s / 1e9 / PCIE_PEAK_GBS, 4), "traffic": None}
+    cfg = {"workload": w.name + ", CPU-offloaded optimizer (state in host memory)", "shard_params": n, "M": w.M,
+           "tensors": len(w.tensors), "host_threads": threads or len(os.sched_getaffinity(0)),
+           "link_bytes_per_param": 6, "link_gbs": round(link, 2), "d2h_copy_gbs": round(d2h_gbs, 2),
+           "host_update_params_per_s": round(host_pps), "hbm_state_bytes_saved": 12 * n, "step_t": hp0["step"],
+           "step_ms_min": round(1e3 * min(per), 3), "step_ms_median": round(1e3 * sorted(per)[S // 2], 3)}
+    return {"value": n / step_s, "ms_per_step": 1e3 * step_s, "config": cfg, "roofline": roofline}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -240,12 +318,14 @@ def main():
         return
     if a.workload is None:
         a.workload = 3 if a.zero2 else 2
+    if a.zero2 and a.offload:
+        sys.exit("bench.py: --zero2 and --offload are separate legs")
     w = workload(a.workload)
     tensors = build_workload(w, a.stagger)
-    if a.zero2:
+    if a.zero2 or a.offload:
         if a.amp:
-            sys.exit("bench.py: --zero2 runs with a fixed loss scale")
-        out = zero2_line(a, w, tensors)
+            sys.exit("bench.py: --zero2 and --offload run with a fixed loss scale")
+        out = zero2_line(a, w, tensors) if a.zero2 else offload_line(a, w, tensors)
         cpu = cpu_baseline(w, a.cpu_sample) if a.cpu_sample > 0 else None
         line = {"metric": METRIC, "value": out["value"], "unit": "params/s", "n_gpus": 1, "steps": a.steps,
                 "warmup": a.warmup, "ms_per_step": out["ms_per_step"], "higher_is_better": True, "scaling": "weak",

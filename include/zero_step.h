@@ -361,10 +361,73 @@ int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_
                           double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
                           hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * CPU-offloaded step (ZeRO-Offload).
+ *
+ * "第2章 软件程序与专用硬件的结合" section 2.3.4 names ZeRO-Offload, which
+ * moves the optimizer state to CPU memory; gsyq.cn/news/457874 section 4.2
+ * configures it (offload_optimizer: device cpu, pin_memory true) and reports
+ * its trade: less GPU memory, a slower step, CPU-GPU transfers of ~20 GB/s.
+ * Here the fp32 master, m and v of the shard live in host memory. The GPU
+ * folds the M replicas, unscales, flags and squares (the first pass of the
+ * two-pass step, into a device fp32 gradient); the gradient goes to pinned
+ * host memory in chunks; host threads apply AdamW to each chunk as it lands
+ * (binary64, the same formula and rounding as the GPU kernels) and emit bf16;
+ * each bf16 chunk goes back to the device shard. The result equals zero_step's
+ * over the same replicas: 4 + 2 bytes per parameter cross the host link
+ * instead of 12 bytes of state living in HBM.
+ * ------------------------------------------------------------------------ */
+
+/* One tensor shard of an offloaded step. Host memory. */
+typedef struct zero_offload_tensor {
+    int64_t n;                /* elements in this shard, >= 0 */
+    const void* const* grads; /* HOST array of M device pointers, n bf16 each (read only) */
+    float* master;            /* HOST memory, n fp32, updated in place */
+    float* exp_avg;           /* HOST memory, n fp32, updated in place */
+    float* exp_avg_sq;        /* HOST memory, n fp32, updated in place */
+    void* param_out;          /* DEVICE, n bf16 codes, written by host-to-device copies */
+} zero_offload_tensor;
+
+/* Device workspace size of zero_offload_step (plan, result record, the fp32
+ * gradient); 0 on invalid arguments. */
+size_t zero_offload_workspace_bytes(const zero_offload_tensor* tensors, int32_t T, int32_t M);
+
+/* Pinned host workspace size of zero_offload_step (staging: 4 bytes of
+ * gradient and 2 bytes of bf16 output per element); 0 on invalid arguments. */
+size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int32_t T);
+
+/*
+ * zero_offload_step -- the step with the optimizer state in host memory.
+ * hp, external_sumsq and the result as for zero_step (*res_host, HOST memory,
+ * is written before the call returns). ws: device workspace of
+ * zero_offload_workspace_bytes(...) bytes, 256-byte aligned (it caches the
+ * call's tables, as for zero_step). host_ws: PINNED host memory
+ * (hipHostMalloc) of zero_offload_host_workspace_bytes(...) bytes, 64-byte
+ * aligned. threads: host threads of the update (0: the size of the process's
+ * CPU affinity mask). The call waits for the GPU's fold and returns once
+ * master, m and v are updated on the host (or the step is skipped); the
+ * bf16 copies into param_out are then enqueued, and `stream` is made to wait
+ * for them, so work later on `stream` sees the new shard. Calls that share a
+ * host workspace must be issued on one stream.
+ */
+int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                      double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                      zero_result* res_host, int32_t threads, hipStream_t stream);
+
+/*
+ * zero_offload_adamw_host -- the host half alone: AdamW on host fp32
+ * master/exp_avg/exp_avg_sq (n each, in place) from the host fp32 gradient g
+ * (multiplied by clip_coef in binary64), bf16 output into host param_out;
+ * hp as for zero_adamw_step; threads as above. For a caller that moves the
+ * gradient itself. Synchronous; launches nothing on the GPU.
+ */
+int zero_offload_adamw_host(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out,
+                            int64_t n, const zero_adamw_hparams* hp, double clip_coef, int32_t threads);
+
 /*
  * zero_workspace_forget -- drop the host-side record that `ws` holds the
- * tensor table of an earlier zero_step, zero_step_amp, zero_bucket_reduce or
- * zero_step_accumulated call. Call it before freeing or
+ * tensor table of an earlier zero_step, zero_step_amp, zero_bucket_reduce,
+ * zero_step_accumulated or zero_offload_step call. Call it before freeing or
  * repurposing such a workspace; the next zero_step on it then rewrites the
  * table. (A workspace whose table was overwritten without this call is
  * detected on the device: zero_result.status = ZERO_ERR_STALE_WORKSPACE and

@@ -20,6 +20,9 @@ Functions keep the C names:
   ``zero_bucket_reduce(shards, flags, grad_scale, stamp, partial, ws)``
 * ``zero_step_accumulated_workspace_bytes(tensors)``,
   ``zero_step_accumulated(tensors, hp, partials, stamp, external_sumsq, ws, res)``
+* ``zero_offload_workspace_bytes(tensors, M)``, ``zero_offload_host_workspace_bytes(tensors)``,
+  ``zero_offload_step(tensors, hp, external_sumsq, ws, host_ws, threads)``,
+  ``zero_offload_adamw_host(master, exp_avg, exp_avg_sq, g, param_out, hp, clip_coef, threads)``
 * ``zero_workspace_forget(ws)``, ``zero_status_string(status)``
 """
 from __future__ import annotations
@@ -52,7 +55,8 @@ EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_gr
            "zero_step_workspace_bytes", "zero_step", "zero_loss_scale_init", "zero_loss_scale_update",
            "zero_step_amp_workspace_bytes", "zero_step_amp", "zero_bucket_reduce_workspace_bytes",
            "zero_bucket_reduce", "zero_step_accumulated_workspace_bytes", "zero_step_accumulated",
-           "zero_workspace_forget", "zero_status_string")
+           "zero_offload_workspace_bytes", "zero_offload_host_workspace_bytes", "zero_offload_step",
+           "zero_offload_adamw_host", "zero_workspace_forget", "zero_status_string")
 LOSS_SCALE_BYTES = 16
 
 
@@ -75,6 +79,16 @@ class _CGradShard(ctypes.Structure):
 class _CAccTensor(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("grad_acc", ctypes.c_void_p), ("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class _COffloadTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class _CResult(ctypes.Structure):
+    _fields_ = [("sumsq", ctypes.c_double), ("clip_coef", ctypes.c_double), ("grad_norm", ctypes.c_float),
+                ("found_inf", ctypes.c_int32), ("skipped", ctypes.c_int32), ("status", ctypes.c_int32)]
 
 
 class _CLossScaleConfig(ctypes.Structure):
@@ -131,6 +145,15 @@ def lib() -> ctypes.CDLL:
         L.zero_step_accumulated.argtypes = [ctypes.POINTER(_CAccTensor), i32, ctypes.POINTER(_CHparams), vp, i32,
                                             u64, dbl, vp, sz, vp, vp]
         L.zero_step_accumulated.restype = ctypes.c_int
+        L.zero_offload_workspace_bytes.argtypes = [ctypes.POINTER(_COffloadTensor), i32, i32]
+        L.zero_offload_workspace_bytes.restype = sz
+        L.zero_offload_host_workspace_bytes.argtypes = [ctypes.POINTER(_COffloadTensor), i32]
+        L.zero_offload_host_workspace_bytes.restype = sz
+        L.zero_offload_step.argtypes = [ctypes.POINTER(_COffloadTensor), i32, i32, ctypes.POINTER(_CHparams), dbl, vp,
+                                        sz, vp, sz, ctypes.POINTER(_CResult), i32, vp]
+        L.zero_offload_step.restype = ctypes.c_int
+        L.zero_offload_adamw_host.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_CHparams), dbl, i32]
+        L.zero_offload_adamw_host.restype = ctypes.c_int
         L.zero_workspace_forget.argtypes = [vp]
         L.zero_workspace_forget.restype = ctypes.c_int
         L.zero_status_string.argtypes = [ctypes.c_int]
@@ -475,6 +498,98 @@ def zero_step_accumulated(tensors: Sequence[AccTensor], hp: HParams, partials: O
     _check(lib().zero_step_accumulated(arr, len(tensors), ctypes.byref(h), _ptr(partials), int(nbuckets),
                                        int(stamp) & (2**64 - 1), float(external_sumsq), _ptr(ws), wsb,
                                        res.data_ptr(), _stream(stream)), "zero_step_accumulated")
+
+
+# ---------------------------------------------------------------- CPU-offloaded step
+
+@dataclasses.dataclass
+class OffloadTensor:
+    """One tensor shard of an offloaded step: M bf16 replicas (device), the
+    fp32 master/exp_avg/exp_avg_sq in host memory (updated in place) and the
+    bf16 output shard (device)."""
+    grads: List[torch.Tensor]
+    master: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    param_out: torch.Tensor
+
+
+def _need_host(t: torch.Tensor, dtype, name: str, n: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cpu":
+        raise ValueError(f"{name}: must be a host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+
+
+def _coffload(tensors: Sequence[OffloadTensor], check: bool):
+    M = len(tensors[0].grads) if tensors else 1
+    keep = []
+    arr = (_COffloadTensor * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        n = t.master.numel()
+        if check:
+            if len(t.grads) != M:
+                raise ValueError(f"tensor {i}: {len(t.grads)} replicas, expected {M}")
+            for r, g in enumerate(t.grads):
+                _need(g, torch.bfloat16, f"tensors[{i}].grads[{r}]", n)
+            for x, nm in ((t.master, "master"), (t.exp_avg, "exp_avg"), (t.exp_avg_sq, "exp_avg_sq")):
+                _need_host(x, torch.float32, f"tensors[{i}].{nm}", n)
+            _need(t.param_out, torch.bfloat16, f"tensors[{i}].param_out", n)
+        ptrs = (ctypes.c_void_p * max(M, 1))(*[g.data_ptr() for g in t.grads])
+        keep.append(ptrs)
+        arr[i] = _COffloadTensor(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), t.master.data_ptr(),
+                                 t.exp_avg.data_ptr(), t.exp_avg_sq.data_ptr(), t.param_out.data_ptr())
+    return arr, keep, M
+
+
+def zero_offload_workspace_bytes(tensors: Sequence[OffloadTensor], M: int) -> int:
+    arr, keep, _ = _coffload(tensors, check=False)
+    return int(lib().zero_offload_workspace_bytes(arr, len(tensors), int(M)))
+
+
+def zero_offload_host_workspace_bytes(tensors: Sequence[OffloadTensor]) -> int:
+    arr, keep, _ = _coffload(tensors, check=False)
+    return int(lib().zero_offload_host_workspace_bytes(arr, len(tensors)))
+
+
+def host_workspace(nbytes: int) -> torch.Tensor:
+    """Pinned host memory of nbytes (page-aligned), for zero_offload_step."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, pin_memory=True)
+
+
+def zero_offload_step(tensors: Sequence[OffloadTensor], hp: HParams, external_sumsq: float, ws: torch.Tensor,
+                      host_ws: torch.Tensor, threads: int = 0, stream=None) -> dict:
+    """Returns the result record (the call reads it on the host)."""
+    _need(ws, torch.uint8, "ws")
+    _need_host(host_ws, torch.uint8, "host_ws")
+    arr, keep, M = _coffload(tensors, check=True)
+    h = hp._c()
+    r = _CResult()
+    _check(lib().zero_offload_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), ws.data_ptr(),
+                                   ws.numel(), host_ws.data_ptr(), host_ws.numel(), ctypes.byref(r), int(threads),
+                                   _stream(stream)), "zero_offload_step")
+    return dict(sumsq=r.sumsq, grad_norm=r.grad_norm, clip_coef=r.clip_coef, found_inf=r.found_inf,
+                skipped=r.skipped, status=r.status)
+
+
+def zero_offload_adamw_host(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, g: torch.Tensor,
+                            param_out: torch.Tensor, hp: HParams, clip_coef: float = 1.0, threads: int = 0) -> None:
+    """The host half of the offloaded step on host tensors (fp32 state and
+    gradient, bf16 output)."""
+    n = master.numel()
+    for t, nm in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (g, "g")):
+        _need_host(t, torch.float32, nm, n)
+    _need_host(param_out, torch.bfloat16, "param_out", n)
+    h = hp._c()
+    _check(lib().zero_offload_adamw_host(master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), g.data_ptr(),
+                                         param_out.data_ptr(), n, ctypes.byref(h), float(clip_coef), int(threads)),
+           "zero_offload_adamw_host")
 
 
 def zero_workspace_forget(ws: torch.Tensor) -> None:

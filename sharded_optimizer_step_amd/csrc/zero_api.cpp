@@ -7,10 +7,12 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <utility>
 #include <vector>
 
+#include "zero_host.h"
 #include "zero_internal.h"
 #include "zero_step.h"
 
@@ -130,6 +132,8 @@ int pick_geom_update(const std::vector<Layout>& layouts, int cus)
 // ------------------------------------------------------------------ plans
 
 bool kind_folds(PlanKind k) { return k != PlanKind::AccStep; }
+// the fp32 gradient of the fold pass is kept in the workspace
+bool kind_keeps_g(PlanKind k) { return k == PlanKind::StepTwoPass || k == PlanKind::Fold; }
 bool kind_updates_after(PlanKind k) { return k == PlanKind::StepTwoPass || k == PlanKind::AccStep; }
 
 PlanOffsets plan_offsets(const std::vector<int64_t>& ns, int32_t M, PlanKind kind)
@@ -140,7 +144,7 @@ PlanOffsets plan_offsets(const std::vector<int64_t>& ns, int32_t M, PlanKind kin
     size_t gbytes = 0;
     for (int64_t n : ns) {
         tiles += tiles_bound(n);
-        if (kind == PlanKind::StepTwoPass && n > 0) gbytes += align_up((static_cast<size_t>(n) + 3) * 4, kAlign);
+        if (kind_keeps_g(kind) && n > 0) gbytes += align_up((static_cast<size_t>(n) + 3) * 4, kAlign);
     }
     const size_t ntiles = static_cast<size_t>(tiles);
     const bool folds = kind_folds(kind);
@@ -189,6 +193,7 @@ struct PlanTensor {
 };
 
 struct Plan {
+    std::vector<float*> gbuf;  // per tensor: the fp32 gradient the fold pass writes (null unless kept)
     PlanOffsets off;
     int geom[2];
     int64_t tiles[2];
@@ -267,7 +272,7 @@ int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void*
         d.tail = L.tail;
         d.ntiles[0] = folds ? layout_tiles(L, tile_vecs[0]) : 0;
         d.ntiles[1] = updates ? layout_tiles(L, tile_vecs[1]) : 0;
-        if (kind == PlanKind::StepTwoPass) {
+        if (kind_keeps_g(kind)) {
             // aligned with the other pointers at element `head`
             const size_t shift = L.nvec >= 0 ? 4u * ((4u - static_cast<unsigned>(L.head) % 4u) % 4u) : 0u;
             d.gbuf = reinterpret_cast<float*>(wsb + gpos + shift);
@@ -300,6 +305,8 @@ int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void*
         auto it = g_plan_cache.find(key);
         cached = it != g_plan_cache.end() && it->second == sig;
     }
+    plan->gbuf.assign(static_cast<size_t>(T), nullptr);
+    for (int32_t t = 0; t < T; ++t) plan->gbuf[t] = desc[t].gbuf;
     plan->off = off;
     plan->geom[0] = geom[0];
     plan->geom[1] = geom[1];
@@ -641,6 +648,252 @@ int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_
     e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, 0, gscale,
                      derive(hp), nullptr, fin, res_dev, stream);
     return hip_status(e);
+}
+
+// ------------------------------------------------------------------ CPU-offloaded step
+
+static HostAdamScalars host_scalars(const zero_adamw_hparams* hp, double coef)
+{
+    const AdamScalars a = derive(hp);
+    return HostAdamScalars{a.b1, a.omb1, a.b2, a.omb2, a.decay, a.lr, a.bc1, a.bc2, a.eps, coef};
+}
+
+static int team_size(int32_t threads) { return threads > 0 ? threads : host_threads_available(); }
+
+}  // extern "C"
+
+namespace {
+
+// Host thread teams, one per size, kept for the life of the process (their
+// threads sleep between calls). A team serves one call at a time: callers
+// hold `use` while they run it.
+struct TeamSlot {
+    std::mutex use;
+    std::unique_ptr<ThreadTeam> team;
+};
+
+TeamSlot& team_slot(int n)
+{
+    static std::mutex mu;
+    static std::map<int, std::unique_ptr<TeamSlot>> slots;
+    std::lock_guard<std::mutex> lk(mu);
+    std::unique_ptr<TeamSlot>& p = slots[n];
+    if (!p) {
+        p.reset(new TeamSlot);
+        p->team.reset(new ThreadTeam(n));
+    }
+    return *p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_offload_adamw_host(float* master, float* exp_avg, float* exp_avg_sq, const float* g, void* param_out,
+                            int64_t n, const zero_adamw_hparams* hp, double clip_coef, int32_t threads)
+{
+    if (n < 0 || !hparams_ok(hp) || threads < 0 || std::isnan(clip_coef)) return ZERO_ERR_INVALID_ARGUMENT;
+    if (n == 0) return ZERO_OK;
+    if (!master || !exp_avg || !exp_avg_sq || !g || !param_out) return ZERO_ERR_INVALID_ARGUMENT;
+    TeamSlot& slot = team_slot(team_size(threads));
+    std::lock_guard<std::mutex> lk(slot.use);
+    host_adamw_parallel(*slot.team, master, exp_avg, exp_avg_sq, g, static_cast<uint16_t*>(param_out), n,
+                        host_scalars(hp, clip_coef));
+    return ZERO_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kOffloadChunk = int64_t(1) << 22;  // elements per transfer-and-update chunk
+constexpr size_t kHostAlign = 64;
+
+// Host staging of an offloaded step: the record, then every tensor's fp32
+// gradient, then every tensor's bf16 output (64-byte aligned regions).
+struct HostLayout {
+    std::vector<size_t> g, out;
+    size_t total;
+};
+
+HostLayout host_layout(const zero_offload_tensor* ts, int32_t T)
+{
+    HostLayout h;
+    size_t pos = kHostAlign;  // the 32-byte result record first
+    for (int32_t t = 0; t < T; ++t) {
+        h.g.push_back(pos);
+        pos = align_up(pos + 4 * static_cast<size_t>(ts[t].n), kHostAlign);
+    }
+    for (int32_t t = 0; t < T; ++t) {
+        h.out.push_back(pos);
+        pos = align_up(pos + 2 * static_cast<size_t>(ts[t].n), kHostAlign);
+    }
+    h.total = pos;
+    return h;
+}
+
+bool offload_tensors_ok(const zero_offload_tensor* ts, int32_t T, int32_t M)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || (T > 0 && ts == nullptr)) return false;
+    for (int32_t t = 0; t < T; ++t)
+        if (ts[t].n < 0) return false;
+    return true;
+}
+
+// One copy stream per device for the host-to-device copies of the bf16
+// shard, so they overlap the device-to-host copies of the gradient.
+hipStream_t copy_stream()
+{
+    static std::mutex mu;
+    static std::map<int, hipStream_t> streams;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = streams.find(dev);
+    if (it != streams.end()) return it->second;
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = s;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t zero_offload_workspace_bytes(const zero_offload_tensor* tensors, int32_t T, int32_t M)
+{
+    if (!offload_tensors_ok(tensors, T, M)) return 0;
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
+    return plan_offsets(ns, M, PlanKind::Fold).total;
+}
+
+size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int32_t T)
+{
+    if (!offload_tensors_ok(tensors, T, 1)) return 0;
+    return host_layout(tensors, T).total;
+}
+
+int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                      double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                      zero_result* res_host, int32_t threads, hipStream_t stream)
+{
+    // ---- arguments (nothing is launched on an error)
+    if (!offload_tensors_ok(tensors, T, M) || !hparams_ok(hp) || res_host == nullptr || threads < 0)
+        return ZERO_ERR_INVALID_ARGUMENT;
+    std::vector<PlanTensor> pts(static_cast<size_t>(T));
+    int64_t total_n = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_offload_tensor& x = tensors[t];
+        pts[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        pts[t].grads = x.grads;  // only the replicas are device memory the fold reads
+        total_n += x.n;
+    }
+    if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    if (host_ws == nullptr || reinterpret_cast<uintptr_t>(host_ws) % kHostAlign != 0)
+        return ZERO_ERR_INVALID_ARGUMENT;
+    const HostLayout hl = host_layout(tensors, T);
+    if (host_ws_bytes < hl.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+    uint8_t* hb = static_cast<uint8_t*>(host_ws);
+    zero_result* rec_h = reinterpret_cast<zero_result*>(hb);
+    zero_result* rec_d = reinterpret_cast<zero_result*>(static_cast<uint8_t*>(ws) + kRecordOffset);
+    const int skip = hp->skip_on_nonfinite != 0;
+
+    // ---- the fold on the GPU, then its record to the host
+    if (total_n == 0) {
+        if (ws_bytes < kAlign) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+        if (launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, rec_d, stream) != hipSuccess)
+            return ZERO_ERR_HIP;
+    } else {
+        Plan plan;
+        const int st = make_plan(pts, M, PlanKind::Fold, ws, ws_bytes, stream, &plan);
+        if (st != ZERO_OK) return st;
+        FinalizeArgs fin{};
+        fin.res = rec_d;
+        fin.counter = plan.counter;
+        fin.external = external_sumsq;
+        fin.max_norm = hp->max_grad_norm;
+        fin.skip = skip;
+        if (launch_fused(Mode::PassA, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
+                         static_cast<float>(hp->grad_scale), AdamScalars{}, plan.parts, fin, nullptr,
+                         stream) != hipSuccess)
+            return ZERO_ERR_HIP;
+        if (hipMemcpyAsync(rec_h, rec_d, sizeof(zero_result), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return ZERO_ERR_HIP;
+        const zero_result rec = *rec_h;
+        if (rec.status != ZERO_OK || rec.skipped != 0) {
+            *res_host = rec;
+            return ZERO_OK;
+        }
+
+        // ---- chunks: gradient down (stream), update on the host, bf16 up (copy stream)
+        struct Chunk {
+            int32_t t;
+            int64_t b, e;
+            hipEvent_t ready;
+        };
+        std::vector<Chunk> chunks;
+        for (int32_t t = 0; t < T; ++t)
+            for (int64_t b = 0; b < tensors[t].n; b += kOffloadChunk)
+                chunks.push_back(Chunk{t, b, std::min(tensors[t].n, b + kOffloadChunk), nullptr});
+        hipStream_t up = copy_stream();
+        if (up == nullptr) return ZERO_ERR_HIP;
+        int status = ZERO_OK;
+        size_t made = 0;
+        for (Chunk& c : chunks) {
+            float* g_h = reinterpret_cast<float*>(hb + hl.g[c.t]) + c.b;
+            if (hipEventCreateWithFlags(&c.ready, hipEventDisableTiming) != hipSuccess) { status = ZERO_ERR_HIP; break; }
+            ++made;
+            if (hipMemcpyAsync(g_h, plan.gbuf[c.t] + c.b, 4 * static_cast<size_t>(c.e - c.b), hipMemcpyDeviceToHost,
+                               stream) != hipSuccess ||
+                hipEventRecord(c.ready, stream) != hipSuccess) {
+                status = ZERO_ERR_HIP;
+                break;
+            }
+        }
+        if (status == ZERO_OK) {
+            TeamSlot& slot = team_slot(team_size(threads));
+            std::lock_guard<std::mutex> lk(slot.use);
+            ThreadTeam& team = *slot.team;
+            const HostAdamScalars sc = host_scalars(hp, rec.clip_coef);
+            for (Chunk& c : chunks) {
+                if (hipEventSynchronize(c.ready) != hipSuccess) { status = ZERO_ERR_HIP; break; }
+                const zero_offload_tensor& x = tensors[c.t];
+                const float* g_h = reinterpret_cast<const float*>(hb + hl.g[c.t]) + c.b;
+                uint16_t* o_h = reinterpret_cast<uint16_t*>(hb + hl.out[c.t]) + c.b;
+                host_adamw_parallel(team, x.master + c.b, x.exp_avg + c.b, x.exp_avg_sq + c.b, g_h, o_h, c.e - c.b,
+                                    sc);
+                if (hipMemcpyAsync(static_cast<uint16_t*>(x.param_out) + c.b, o_h, 2 * static_cast<size_t>(c.e - c.b),
+                                   hipMemcpyHostToDevice, up) != hipSuccess) {
+                    status = ZERO_ERR_HIP;
+                    break;
+                }
+            }
+        }
+        // the caller's stream waits for the bf16 shard; then the events go
+        hipEvent_t done = nullptr;
+        if (status == ZERO_OK) {
+            if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess ||
+                hipEventRecord(done, up) != hipSuccess || hipStreamWaitEvent(stream, done, 0) != hipSuccess)
+                status = ZERO_ERR_HIP;
+        }
+        if (done != nullptr) (void)hipEventDestroy(done);
+        for (size_t i = 0; i < made; ++i) (void)hipEventDestroy(chunks[i].ready);
+        if (status != ZERO_OK) return status;
+        *res_host = rec;
+        return ZERO_OK;
+    }
+    if (hipMemcpyAsync(rec_h, rec_d, sizeof(zero_result), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return ZERO_ERR_HIP;
+    *res_host = *rec_h;
+    return ZERO_OK;
 }
 
 int zero_workspace_forget(const void* ws)

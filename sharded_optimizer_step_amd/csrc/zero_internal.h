@@ -107,11 +107,14 @@ struct alignas(16) PlanHeader {
 
 // What a workspace plan drives: the fused step (one or two passes), the
 // accumulation of one gradient bucket, or the step from accumulated gradients.
-enum class PlanKind : int32_t { Step = 0, StepTwoPass = 1, Bucket = 2, AccStep = 3 };
+enum class PlanKind : int32_t { Step = 0, StepTwoPass = 1, Bucket = 2, AccStep = 3, Fold = 4 };
 
 // Byte offset, in the 256-byte header region of a zero_step workspace, of the
 // arrival counter of the fold pass (zero between launches).
 constexpr size_t kCounterOffset = 128;
+// Byte offset, in the same region, of the device result record that a
+// fold-only plan (the CPU-offloaded step) writes.
+constexpr size_t kRecordOffset = 192;
 
 // What the last workgroup of a fold pass needs to write the result record
 // and, in the AMP form (ls non-null), to move the loss scale.

@@ -49,7 +49,8 @@ def test_struct_layouts_match_header(tmp_path):
     import subprocess
     fields = {"zero_adamw_hparams": z._CHparams, "zero_tensor": z._CTensor,
               "zero_loss_scale_config": z._CLossScaleConfig, "zero_grad_shard": z._CGradShard,
-              "zero_acc_tensor": z._CAccTensor}
+              "zero_acc_tensor": z._CAccTensor, "zero_offload_tensor": z._COffloadTensor,
+              "zero_result": z._CResult}
     body = []
     for cname, cls in fields.items():
         body.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -285,3 +286,41 @@ def test_step_accumulated_argument_checks():
     arr3[0] = z._CAccTensor(-1, None, None, None, None, None)
     assert L.zero_step_accumulated_workspace_bytes(arr3, 1) == 0
     assert L.zero_step_accumulated(arr3, 1, ctypes.byref(h), parts, 1, 0, 0.0, ws, need, res, None) == 1
+
+
+def _offload(n=100, M=2):
+    ptrs = (ctypes.c_void_p * M)(*[256 * (r + 1) for r in range(M)])
+    arr = (z._COffloadTensor * 1)()
+    arr[0] = z._COffloadTensor(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    return arr, ptrs
+
+
+def test_offload_step_argument_checks():
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    arr, keep = _offload()
+    need = L.zero_offload_workspace_bytes(arr, 1, 2)
+    hneed = L.zero_offload_host_workspace_bytes(arr, 1)
+    assert need > 4 * 100 and hneed >= 6 * 100   # the fp32 gradient on the device; g and bf16 staged on the host
+    res = z._CResult()
+    ws, hw = 1 << 24, 1 << 25
+    call = lambda a=arr, T=1, M=2, hp=h, w=ws, wb=need, hws=hw, hb=hneed, r=ctypes.byref(res), th=0: \
+        L.zero_offload_step(a, T, M, ctypes.byref(hp), 0.0, w, wb, hws, hb, r, th, None)
+    assert call(r=None) == 1                       # no result
+    assert call(th=-1) == 1                        # negative thread count
+    assert call(M=0) == 1
+    assert call(T=-1) == 1
+    assert call(hp=_hp(step=0)) == 1
+    assert call(w=None) == 1 and call(w=ws + 16) == 1          # no / misaligned device workspace
+    assert call(hws=None) == 1 and call(hws=hw + 8) == 1       # no / misaligned host workspace
+    assert call(hb=hneed - 1) == 2                             # host workspace short
+    assert call(wb=need - 1) == 2                              # device workspace short
+    nul = (ctypes.c_void_p * 2)(256, None)
+    arr2 = (z._COffloadTensor * 1)()
+    arr2[0] = z._COffloadTensor(100, ctypes.cast(nul, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    assert call(a=arr2) == 1                                   # a null replica
+    arr3, k3 = _offload()
+    arr3[0].exp_avg = None
+    assert call(a=arr3) == 1                                   # no host state
+    neg, k4 = _offload(n=-1)
+    assert L.zero_offload_workspace_bytes(neg, 1, 2) == 0 and L.zero_offload_host_workspace_bytes(neg, 1) == 0

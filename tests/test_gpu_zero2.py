@@ -3,8 +3,8 @@ zero_step_accumulated) against the CPU oracle, through the C ABI.
 
 Gates: the fp32 accumulator bit-exact after every micro-batch (the fold and
 the running sum are fixed-order binary32); found_inf bit-exact; the bucket
-partial's sum of squares within 1e-12 relative of the oracle's index-order
-sum; master/m/v within max(2e-6 |ref|, 1e-7); the bf16 output within 1 ulp;
+partial's sum of squares within the oracle's own error bound for its
+index-order binary64 sum (sumsq_tol); master/m/v within max(2e-6 |ref|, 1e-7); the bf16 output within 1 ulp;
 the norm within 1e-5 relative."""
 import math
 
