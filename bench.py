@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--zero2", action="store_true",
                    help="the ZeRO-2 streaming step: per-bucket zero_bucket_reduce, then zero_step_accumulated")
     p.add_argument("--micro-batches", type=int, default=1, help="--zero2: micro-batches accumulated per step")
+    p.add_argument("--streams", type=int, default=2,
+                   help="--zero2: side streams the bucket reduces alternate over (1: the launch stream)")
     p.add_argument("--offload", action="store_true",
                    help="the CPU-offloaded step: zero_offload_step with the optimizer state in host memory")
     p.add_argument("--threads", type=int, default=0, help="--offload: host threads (0: the CPU affinity mask)")
@@ -171,14 +173,25 @@ def zero2_line(a, w, tensors) -> dict:
     hp = z.HParams(**hp0)
     res = z.new_result()
     stream = torch.cuda.current_stream()
+    # buckets are independent (own accumulators, workspace and partial), so a
+    # loop that overlaps communication issues them on side streams; bucket b
+    # always goes to the same one, which orders its micro-batches
+    NS = max(1, a.streams)
+    side = [torch.cuda.Stream() for _ in range(NS)] if NS > 1 else [stream]
 
     def step(i, ev=None):
         hp.step = hp0["step"] + i
         stamp = i + 1
+        if NS > 1:
+            for sd in side:
+                sd.wait_stream(stream)
         for k in range(K):
             flags = (z.BUCKET_ACCUMULATE if k else 0) | (z.BUCKET_FINAL if k == K - 1 else 0)
-            for rd in reducers:
-                rd.reduce(flags, hp.grad_scale, stamp, stream)
+            for b, rd in enumerate(reducers):
+                rd.reduce(flags, hp.grad_scale, stamp, side[b % NS])
+        if NS > 1:
+            for sd in side:
+                stream.wait_stream(sd)
         if ev is not None:
             ev.record(stream)
         z.zero_step_accumulated(ats, hp, parts, len(buckets), stamp, 0.0, sws, res, stream)
@@ -221,6 +234,7 @@ def zero2_line(a, w, tensors) -> dict:
     cfg = {"workload": w.name + f", ZeRO-2 streaming: {len(buckets)} buckets of reduce_bucket_size 5e7 "
                                 f"in backward order, {K} micro-batch(es)",
            "shard_params": n, "M": w.M, "tensors": len(w.tensors), "buckets": len(buckets), "micro_batches": K,
+           "reduce_streams": NS,
            "bytes_per_param": bpp, "step_t": hp0["step"],
            "hbm_gbs": round(bpp * n / (avg_ms * 1e-3) / 1e9, 1),
            "reduce_ms": round(reduce_ms, 4), "reduce_gbs": round(b_reduce * n / (reduce_ms * 1e-3) / 1e9, 1),
