@@ -408,7 +408,9 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
  * master, m and v are updated on the host (or the step is skipped); the
  * bf16 copies into param_out are then enqueued, and `stream` is made to wait
  * for them, so work later on `stream` sees the new shard. Calls that share a
- * host workspace must be issued on one stream.
+ * host workspace must be issued on one stream. Argument errors are reported
+ * before anything is launched; a HIP error during the transfers
+ * (ZERO_ERR_HIP) can leave the host state partly updated.
  */
 int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
                       double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
