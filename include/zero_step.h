@@ -339,6 +339,18 @@ int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int3
                        hipStream_t stream);
 
 /*
+ * zero_bucket_reduce_amp -- zero_bucket_reduce under the dynamic loss scale
+ * ls_dev (device): the final pass squares acc * (fl32(grad_scale) *
+ * inv_scale), the binary32 product read from ls_dev on the device, and
+ * stores that product in the partial's grad_scale. ls_dev is only read; it
+ * must not move between a bucket's final pass and the step that consumes the
+ * partials (zero_step_accumulated_amp moves it at the end of the step).
+ */
+int zero_bucket_reduce_amp(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                           const zero_loss_scale* ls_dev, uint64_t stamp, zero_bucket_partial* partial_dev, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * zero_step_accumulated_workspace_bytes -- workspace size for
  * zero_step_accumulated over this tensor list; 0 on invalid arguments.
  */
@@ -360,6 +372,21 @@ int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_
                           const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
                           double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
                           hipStream_t stream);
+
+/*
+ * zero_step_accumulated_amp -- zero_step_accumulated under the dynamic loss
+ * scale ls_dev (device, with its config cfg): the multiplier is
+ * fl32(hp->grad_scale) * inv_scale read on the device (the partials must
+ * carry that product, as zero_bucket_reduce_amp writes it); a step with any
+ * inf/NaN is always skipped (skip_on_nonfinite is ignored); after the update
+ * the state moves on the step's found_inf (one more small launch). Workspace
+ * as for zero_step_accumulated.
+ */
+int zero_step_accumulated_amp(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                              const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev,
+                              const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                              double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
+                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * CPU-offloaded step (ZeRO-Offload).
@@ -415,6 +442,19 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
 int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
                       double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
                       zero_result* res_host, int32_t threads, hipStream_t stream);
+
+/*
+ * zero_offload_step_amp -- zero_offload_step under the dynamic loss scale
+ * ls_dev (device, with its config cfg): the GPU's fold multiplies by
+ * fl32(hp->grad_scale) * inv_scale read on the device, a step with any inf/NaN
+ * is always skipped, and the fold's last workgroup moves the state, as in
+ * zero_step_amp; the host update is unchanged. Workspaces as for
+ * zero_offload_step.
+ */
+int zero_offload_step_amp(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                          const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, double external_sumsq, void* ws,
+                          size_t ws_bytes, void* host_ws, size_t host_ws_bytes, zero_result* res_host,
+                          int32_t threads, hipStream_t stream);
 
 /*
  * zero_offload_adamw_host -- the host half alone: AdamW on host fp32

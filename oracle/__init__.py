@@ -335,6 +335,18 @@ def zero_step_amp(tensors: Sequence[TensorState], hp: HParams, cfg: LossScaleCon
     return new, res, loss_scale_update(state, cfg, res.found_inf)
 
 
+def zero_step_accumulated_amp(accs: Sequence[np.ndarray], tensors: Sequence[TensorState], hp: HParams,
+                              cfg: LossScaleConfig, state: LossScale, external_sumsq: float = 0.0):
+    """The ZeRO-2 step from accumulated gradients under a dynamic loss scale:
+    the multiplier is grad_scale x inv_scale (a binary32 product), a step with
+    a non-finite gradient is skipped, then the scale moves on the step's flag.
+    Returns (new TensorStates, Result, new LossScale)."""
+    mult = float(np.float32(hp.grad_scale) * np.float32(state.inv_scale))
+    h = dataclasses.replace(hp, grad_scale=mult, skip_on_nonfinite=1)
+    new, res = zero_step_accumulated(accs, tensors, h, external_sumsq)
+    return new, res, loss_scale_update(state, cfg, res.found_inf)
+
+
 # --------------------------------------------------------------------------
 # Memory accounting of mixed-precision AdamW training state
 # ([CS336 L7] "训练内存的详细分析": bf16 parameter 2 B, bf16 gradient 2 B,

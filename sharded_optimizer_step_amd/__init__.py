@@ -56,7 +56,8 @@ EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_gr
            "zero_step_amp_workspace_bytes", "zero_step_amp", "zero_bucket_reduce_workspace_bytes",
            "zero_bucket_reduce", "zero_step_accumulated_workspace_bytes", "zero_step_accumulated",
            "zero_offload_workspace_bytes", "zero_offload_host_workspace_bytes", "zero_offload_step",
-           "zero_offload_adamw_host", "zero_workspace_forget", "zero_status_string")
+           "zero_offload_adamw_host", "zero_bucket_reduce_amp", "zero_step_accumulated_amp",
+           "zero_offload_step_amp", "zero_workspace_forget", "zero_status_string")
 LOSS_SCALE_BYTES = 16
 
 
@@ -154,6 +155,15 @@ def lib() -> ctypes.CDLL:
         L.zero_offload_step.restype = ctypes.c_int
         L.zero_offload_adamw_host.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_CHparams), dbl, i32]
         L.zero_offload_adamw_host.restype = ctypes.c_int
+        lsc = ctypes.POINTER(_CLossScaleConfig)
+        L.zero_bucket_reduce_amp.argtypes = [ctypes.POINTER(_CGradShard), i32, i32, i32, dbl, vp, u64, vp, vp, sz, vp]
+        L.zero_bucket_reduce_amp.restype = ctypes.c_int
+        L.zero_step_accumulated_amp.argtypes = [ctypes.POINTER(_CAccTensor), i32, ctypes.POINTER(_CHparams), lsc, vp,
+                                                vp, i32, u64, dbl, vp, sz, vp, vp]
+        L.zero_step_accumulated_amp.restype = ctypes.c_int
+        L.zero_offload_step_amp.argtypes = [ctypes.POINTER(_COffloadTensor), i32, i32, ctypes.POINTER(_CHparams), lsc,
+                                            vp, dbl, vp, sz, vp, sz, ctypes.POINTER(_CResult), i32, vp]
+        L.zero_offload_step_amp.restype = ctypes.c_int
         L.zero_workspace_forget.argtypes = [vp]
         L.zero_workspace_forget.restype = ctypes.c_int
         L.zero_status_string.argtypes = [ctypes.c_int]
@@ -444,7 +454,8 @@ class BucketReducer:
     prepared here and no per-call Python checks. The shards' tensors, the
     partial and the workspace must stay alive and at the same addresses."""
 
-    def __init__(self, shards: Sequence[GradShard], partial: Optional[torch.Tensor], ws: Optional[torch.Tensor] = None):
+    def __init__(self, shards: Sequence[GradShard], partial: Optional[torch.Tensor], ws: Optional[torch.Tensor] = None,
+                 ls: Optional[torch.Tensor] = None):
         self._arr, self._keep, self.M = _cshards(shards, check=True)
         self._shards = list(shards)
         self.T = len(self._shards)
@@ -457,13 +468,32 @@ class BucketReducer:
         self._wsp = _ptr(ws)
         self._wsb = ws.numel() * ws.element_size() if ws is not None else 0
         self._pp = _ptr(partial)
-        self._fn = lib().zero_bucket_reduce
+        if ls is not None:
+            _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+        self._ls = ls  # AMP: the dynamic loss scale the final pass reads
+        self._fn = lib().zero_bucket_reduce if ls is None else lib().zero_bucket_reduce_amp
 
     def reduce(self, flags: int, grad_scale: float, stamp: int, stream=None) -> None:
-        st = self._fn(self._arr, self.T, self.M, flags, grad_scale, stamp & 0xFFFFFFFFFFFFFFFF, self._pp, self._wsp,
-                      self._wsb, _stream(stream))
+        if self._ls is None:
+            st = self._fn(self._arr, self.T, self.M, flags, grad_scale, stamp & 0xFFFFFFFFFFFFFFFF, self._pp,
+                          self._wsp, self._wsb, _stream(stream))
+        else:
+            st = self._fn(self._arr, self.T, self.M, flags, grad_scale, self._ls.data_ptr(),
+                          stamp & 0xFFFFFFFFFFFFFFFF, self._pp, self._wsp, self._wsb, _stream(stream))
         if st != ZERO_OK:
             raise ZeroError(st, "zero_bucket_reduce")
+
+
+def zero_bucket_reduce_amp(shards: Sequence[GradShard], flags: int, grad_scale: float, ls: torch.Tensor, stamp: int,
+                           partial: Optional[torch.Tensor], ws: Optional[torch.Tensor], stream=None) -> None:
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    if partial is not None:
+        _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
+    arr, keep, M = _cshards(shards, check=True)
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_bucket_reduce_amp(arr, len(shards), M, int(flags), float(grad_scale), ls.data_ptr(),
+                                        int(stamp) & (2**64 - 1), _ptr(partial), _ptr(ws), wsb, _stream(stream)),
+           "zero_bucket_reduce_amp")
 
 
 def _cacc(tensors: Sequence[AccTensor], check: bool):
@@ -590,6 +620,43 @@ def zero_offload_adamw_host(master: torch.Tensor, exp_avg: torch.Tensor, exp_avg
     _check(lib().zero_offload_adamw_host(master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), g.data_ptr(),
                                          param_out.data_ptr(), n, ctypes.byref(h), float(clip_coef), int(threads)),
            "zero_offload_adamw_host")
+
+
+def zero_step_accumulated_amp(tensors: Sequence[AccTensor], hp: HParams, cfg: "LossScaleConfig", ls: torch.Tensor,
+                              partials: Optional[torch.Tensor], nbuckets: int, stamp: int, external_sumsq: float,
+                              ws: Optional[torch.Tensor], res: torch.Tensor, stream=None) -> None:
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    if nbuckets > 0:
+        _need(partials, torch.uint8, "partials")
+        if partials.numel() < nbuckets * BUCKET_PARTIAL_BYTES:
+            raise ValueError(f"partials: {partials.numel()} bytes for {nbuckets} buckets")
+    arr = _cacc(tensors, check=True)
+    h = hp._c()
+    c = cfg._c()
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().zero_step_accumulated_amp(arr, len(tensors), ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
+                                           _ptr(partials), int(nbuckets), int(stamp) & (2**64 - 1),
+                                           float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
+           "zero_step_accumulated_amp")
+
+
+def zero_offload_step_amp(tensors: Sequence[OffloadTensor], hp: HParams, cfg: "LossScaleConfig", ls: torch.Tensor,
+                          external_sumsq: float, ws: torch.Tensor, host_ws: torch.Tensor, threads: int = 0,
+                          stream=None) -> dict:
+    _need(ws, torch.uint8, "ws")
+    _need_host(host_ws, torch.uint8, "host_ws")
+    _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
+    arr, keep, M = _coffload(tensors, check=True)
+    h = hp._c()
+    c = cfg._c()
+    r = _CResult()
+    _check(lib().zero_offload_step_amp(arr, len(tensors), M, ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
+                                       float(external_sumsq), ws.data_ptr(), ws.numel(), host_ws.data_ptr(),
+                                       host_ws.numel(), ctypes.byref(r), int(threads), _stream(stream)),
+           "zero_offload_step_amp")
+    return dict(sumsq=r.sumsq, grad_norm=r.grad_norm, clip_coef=r.clip_coef, found_inf=r.found_inf,
+                skipped=r.skipped, status=r.status)
 
 
 def zero_workspace_forget(ws: torch.Tensor) -> None:

@@ -397,14 +397,16 @@ int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     fin.max_norm = hp->max_grad_norm;
     fin.skip = skip;
     fin.ls = ls;
+    fin.scale_from = ls;
     if (amp) fin.lscfg = *lscfg;
     hipError_t e = launch_fused(first_mode, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
                                 gscale, c, plan.parts, fin, nullptr, stream);
     if (e != hipSuccess) return ZERO_ERR_HIP;
     if (two_pass) {
         // the stored gradient is already scaled
+        FinalizeArgs none{};
         e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, M, 1.0f,
-                         c, plan.parts, fin, res_dev, stream);
+                         c, plan.parts, none, res_dev, stream);
         if (e != hipSuccess) return ZERO_ERR_HIP;
     }
     return ZERO_OK;
@@ -559,9 +561,13 @@ size_t zero_bucket_reduce_workspace_bytes(const zero_grad_shard* shards, int32_t
     return plan_offsets(ns, M, PlanKind::Bucket).total;
 }
 
-int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
-                       uint64_t stamp, zero_bucket_partial* partial_dev, void* ws, size_t ws_bytes,
-                       hipStream_t stream)
+}  // extern "C"
+
+// The bucket reduce; ls non-null for the AMP form (the final pass squares
+// acc * fl32(grad_scale) * ls->inv_scale).
+static int bucket_impl(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                       const zero_loss_scale* ls, uint64_t stamp, zero_bucket_partial* partial_dev, void* ws,
+                       size_t ws_bytes, hipStream_t stream)
 {
     if (T < 0 || M < 1 || M > ZERO_MAX_RANKS) return ZERO_ERR_INVALID_ARGUMENT;
     if ((flags & ~(ZERO_BUCKET_ACCUMULATE | ZERO_BUCKET_FINAL)) != 0) return ZERO_ERR_INVALID_ARGUMENT;
@@ -585,18 +591,36 @@ int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int3
     }
     const float gscale = final ? static_cast<float>(grad_scale) : 1.0f;
     if (total_n == 0)
-        return final ? hip_status(launch_bucket_partial_empty(partial_dev, stamp, gscale, stream)) : ZERO_OK;
+        return final ? hip_status(launch_bucket_partial_empty(partial_dev, stamp, gscale, ls, stream)) : ZERO_OK;
     Plan plan;
     const int st = make_plan(pts, M, PlanKind::Bucket, ws, ws_bytes, stream, &plan);
     if (st != ZERO_OK) return st;
     FinalizeArgs fin{};
     fin.counter = plan.counter;
+    fin.scale_from = final ? ls : nullptr;
     fin.slot = partial_dev;
     fin.stamp = stamp;
     fin.accumulate = (flags & ZERO_BUCKET_ACCUMULATE) != 0;
     fin.final = final;
     return hip_status(launch_fused(Mode::Acc, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig,
                                    M, gscale, AdamScalars{}, plan.parts, fin, nullptr, stream));
+}
+
+extern "C" {
+
+int zero_bucket_reduce(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                       uint64_t stamp, zero_bucket_partial* partial_dev, void* ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    return bucket_impl(shards, T, M, flags, grad_scale, nullptr, stamp, partial_dev, ws, ws_bytes, stream);
+}
+
+int zero_bucket_reduce_amp(const zero_grad_shard* shards, int32_t T, int32_t M, int32_t flags, double grad_scale,
+                           const zero_loss_scale* ls_dev, uint64_t stamp, zero_bucket_partial* partial_dev, void* ws,
+                           size_t ws_bytes, hipStream_t stream)
+{
+    if (ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    return bucket_impl(shards, T, M, flags, grad_scale, ls_dev, stamp, partial_dev, ws, ws_bytes, stream);
 }
 
 static bool acc_tensors_ok(const zero_acc_tensor* tensors, int32_t T)
@@ -615,10 +639,15 @@ size_t zero_step_accumulated_workspace_bytes(const zero_acc_tensor* tensors, int
     return plan_offsets(ns, 0, PlanKind::AccStep).total;
 }
 
-int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
-                          const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
-                          double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
-                          hipStream_t stream)
+}  // extern "C"
+
+// The step from accumulated gradients; lscfg/ls non-null for the AMP form:
+// the multiplier reads ls->inv_scale on the device, a non-finite gradient
+// always skips, and the scale moves once the update has read it.
+static int acc_step_impl(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                         const zero_loss_scale_config* lscfg, zero_loss_scale* ls,
+                         const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                         double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
 {
     if (!acc_tensors_ok(tensors, T) || !hparams_ok(hp) || res_dev == nullptr || nbuckets < 0)
         return ZERO_ERR_INVALID_ARGUMENT;
@@ -634,20 +663,48 @@ int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_
         total_n += x.n;
     }
     const float gscale = static_cast<float>(hp->grad_scale);
-    const int skip = hp->skip_on_nonfinite != 0;
-    if (total_n == 0)
-        return hip_status(launch_bucket_finalize(nullptr, 0, partials_dev, nbuckets, stamp, gscale, external_sumsq,
-                                                 hp->max_grad_norm, skip, res_dev, stream));
-    Plan plan;
-    const int st = make_plan(pts, 0, PlanKind::AccStep, ws, ws_bytes, stream, &plan);
-    if (st != ZERO_OK) return st;
-    hipError_t e = launch_bucket_finalize(plan.hdr, plan.sig, partials_dev, nbuckets, stamp, gscale, external_sumsq,
-                                          hp->max_grad_norm, skip, res_dev, stream);
-    if (e != hipSuccess) return ZERO_ERR_HIP;
-    FinalizeArgs fin{};
-    e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, 0, gscale,
-                     derive(hp), nullptr, fin, res_dev, stream);
+    const bool amp = ls != nullptr;
+    const int skip = amp || hp->skip_on_nonfinite != 0;
+    hipError_t e;
+    if (total_n == 0) {
+        e = launch_bucket_finalize(nullptr, 0, partials_dev, nbuckets, stamp, gscale, ls, external_sumsq,
+                                   hp->max_grad_norm, skip, res_dev, stream);
+    } else {
+        Plan plan;
+        const int st = make_plan(pts, 0, PlanKind::AccStep, ws, ws_bytes, stream, &plan);
+        if (st != ZERO_OK) return st;
+        e = launch_bucket_finalize(plan.hdr, plan.sig, partials_dev, nbuckets, stamp, gscale, ls, external_sumsq,
+                                   hp->max_grad_norm, skip, res_dev, stream);
+        if (e != hipSuccess) return ZERO_ERR_HIP;
+        FinalizeArgs fin{};
+        fin.scale_from = ls;
+        e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, 0,
+                         gscale, derive(hp), nullptr, fin, res_dev, stream);
+    }
+    if (e == hipSuccess && amp) e = launch_loss_scale_update(*lscfg, res_dev, ls, stream);
     return hip_status(e);
+}
+
+extern "C" {
+
+int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                          const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                          double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
+                          hipStream_t stream)
+{
+    return acc_step_impl(tensors, T, hp, nullptr, nullptr, partials_dev, nbuckets, stamp, external_sumsq, ws,
+                         ws_bytes, res_dev, stream);
+}
+
+int zero_step_accumulated_amp(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
+                              const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev,
+                              const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
+                              double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev,
+                              hipStream_t stream)
+{
+    if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    return acc_step_impl(tensors, T, hp, cfg, ls_dev, partials_dev, nbuckets, stamp, external_sumsq, ws, ws_bytes,
+                         res_dev, stream);
 }
 
 // ------------------------------------------------------------------ CPU-offloaded step
@@ -775,9 +832,15 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
     return host_layout(tensors, T).total;
 }
 
-int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
-                      double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
-                      zero_result* res_host, int32_t threads, hipStream_t stream)
+}  // extern "C"
+
+// The offloaded step; lscfg/ls non-null for the AMP form: the fold reads
+// ls->inv_scale, always skips on a non-finite gradient, and its last
+// workgroup moves the scale (the stored gradient is already unscaled).
+static int offload_impl(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                        const zero_loss_scale_config* lscfg, zero_loss_scale* ls, double external_sumsq, void* ws,
+                        size_t ws_bytes, void* host_ws, size_t host_ws_bytes, zero_result* res_host,
+                        int32_t threads, hipStream_t stream)
 {
     // ---- arguments (nothing is launched on an error)
     if (!offload_tensors_ok(tensors, T, M) || !hparams_ok(hp) || res_host == nullptr || threads < 0)
@@ -802,13 +865,15 @@ int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, 
     uint8_t* hb = static_cast<uint8_t*>(host_ws);
     zero_result* rec_h = reinterpret_cast<zero_result*>(hb);
     zero_result* rec_d = reinterpret_cast<zero_result*>(static_cast<uint8_t*>(ws) + kRecordOffset);
-    const int skip = hp->skip_on_nonfinite != 0;
+    const bool amp = ls != nullptr;
+    const int skip = amp || hp->skip_on_nonfinite != 0;
 
     // ---- the fold on the GPU, then its record to the host
     if (total_n == 0) {
         if (ws_bytes < kAlign) return ZERO_ERR_WORKSPACE_TOO_SMALL;
         if (launch_finalize(nullptr, 0, external_sumsq, hp->max_grad_norm, skip, rec_d, stream) != hipSuccess)
             return ZERO_ERR_HIP;
+        if (amp && launch_loss_scale_update(*lscfg, rec_d, ls, stream) != hipSuccess) return ZERO_ERR_HIP;
     } else {
         Plan plan;
         const int st = make_plan(pts, M, PlanKind::Fold, ws, ws_bytes, stream, &plan);
@@ -819,6 +884,9 @@ int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, 
         fin.external = external_sumsq;
         fin.max_norm = hp->max_grad_norm;
         fin.skip = skip;
+        fin.ls = ls;
+        fin.scale_from = ls;
+        if (amp) fin.lscfg = *lscfg;
         if (launch_fused(Mode::PassA, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
                          static_cast<float>(hp->grad_scale), AdamScalars{}, plan.parts, fin, nullptr,
                          stream) != hipSuccess)
@@ -894,6 +962,26 @@ int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, 
         return ZERO_ERR_HIP;
     *res_host = *rec_h;
     return ZERO_OK;
+}
+
+extern "C" {
+
+int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                      double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                      zero_result* res_host, int32_t threads, hipStream_t stream)
+{
+    return offload_impl(tensors, T, M, hp, nullptr, nullptr, external_sumsq, ws, ws_bytes, host_ws, host_ws_bytes,
+                        res_host, threads, stream);
+}
+
+int zero_offload_step_amp(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                          const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, double external_sumsq, void* ws,
+                          size_t ws_bytes, void* host_ws, size_t host_ws_bytes, zero_result* res_host,
+                          int32_t threads, hipStream_t stream)
+{
+    if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    return offload_impl(tensors, T, M, hp, cfg, ls_dev, external_sumsq, ws, ws_bytes, host_ws, host_ws_bytes,
+                        res_host, threads, stream);
 }
 
 int zero_workspace_forget(const void* ws)

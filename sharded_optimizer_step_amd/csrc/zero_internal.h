@@ -124,8 +124,9 @@ struct FinalizeArgs {
     double external;
     double max_norm;
     int skip;
-    zero_loss_scale* ls;           // null unless AMP; the fold also reads its inv_scale
+    zero_loss_scale* ls;           // non-null (AMP): the fold's last workgroup moves this loss scale
     zero_loss_scale_config lscfg;  // meaningful when ls is non-null
+    const zero_loss_scale* scale_from;  // non-null (AMP): the multiplier is gscale * scale_from->inv_scale
     // bucket accumulation (Mode::Acc): the last workgroup of a final pass
     // writes the bucket partial instead of a result record
     zero_bucket_partial* slot;
@@ -172,13 +173,16 @@ hipError_t launch_adamw(float* master, float* m, float* v, const float* g, uint1
 hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external, double max_norm, int skip,
                            zero_result* res, hipStream_t s);
 // The bucket partials of a ZeRO-2 step combined in index order into the
-// result record, each checked against the step's stamp and fp32 scale; a
-// stale plan `hdr` (may be null) is reported instead.
+// result record, each checked against the step's stamp and fp32 multiplier
+// (scale, times ls->inv_scale when ls is non-null); a stale plan `hdr` (may
+// be null) is reported instead.
 hipError_t launch_bucket_finalize(const PlanHeader* hdr, uint64_t sig, const zero_bucket_partial* parts, int32_t nb,
-                                  uint64_t stamp, float scale, double external, double max_norm, int skip,
-                                  zero_result* res, hipStream_t s);
-// The partial of a final bucket pass over no elements.
-hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale, hipStream_t s);
+                                  uint64_t stamp, float scale, const zero_loss_scale* ls, double external,
+                                  double max_norm, int skip, zero_result* res, hipStream_t s);
+// The partial of a final bucket pass over no elements (scale times
+// ls->inv_scale when ls is non-null).
+hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale,
+                                       const zero_loss_scale* ls, hipStream_t s);
 hipError_t launch_loss_scale_init(const zero_loss_scale& s, zero_loss_scale* ls, hipStream_t st);
 hipError_t launch_loss_scale_update(const zero_loss_scale_config& c, const zero_result* res, zero_loss_scale* ls,
                                     hipStream_t st);

@@ -715,9 +715,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
         if (res->skipped != 0 || res->status != 0) return;
         coef = res->clip_coef;
     }
-    if constexpr (MODE == Mode::Full || MODE == Mode::PassA) {
-        if (fin.ls != nullptr) gscale = gscale * fin.ls->inv_scale;  // AMP: the scale of this step
-    }
+    if (fin.scale_from != nullptr) gscale = gscale * fin.scale_from->inv_scale;  // AMP: the scale of this step
     constexpr Op OP = MODE == Mode::Full    ? Op::Full
                       : MODE == Mode::PassA ? Op::PassA
                       : MODE == Mode::Acc   ? Op::Acc
@@ -776,9 +774,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const Partial* __res
 __global__ __launch_bounds__(kThreads) void bucket_finalize_kernel(const PlanHeader* __restrict__ hdr, uint64_t sig,
                                                                    const zero_bucket_partial* __restrict__ parts,
                                                                    int32_t nb, uint64_t stamp, float scale,
+                                                                   const zero_loss_scale* __restrict__ ls,
                                                                    double external, double max_norm, int skip,
                                                                    zero_result* __restrict__ res)
 {
+    if (ls != nullptr) scale = scale * ls->inv_scale;  // AMP: the multiplier the buckets were squared with
     if (hdr != nullptr && hdr->signature != sig) {
         if (threadIdx.x == 0) *res = stale_record();
         return;
@@ -797,9 +797,10 @@ __global__ __launch_bounds__(kThreads) void bucket_finalize_kernel(const PlanHea
                             : make_record(sumsq, flags & 1u, external, max_norm, skip);
 }
 
-__global__ void bucket_partial_empty_kernel(zero_bucket_partial* __restrict__ slot, uint64_t stamp, float scale)
+__global__ void bucket_partial_empty_kernel(zero_bucket_partial* __restrict__ slot, uint64_t stamp, float scale,
+                                            const zero_loss_scale* __restrict__ ls)
 {
-    if (threadIdx.x == 0) *slot = bucket_partial(0.0, 0, stamp, scale);
+    if (threadIdx.x == 0) *slot = bucket_partial(0.0, 0, stamp, ls != nullptr ? scale * ls->inv_scale : scale);
 }
 
 __global__ void loss_scale_init_kernel(zero_loss_scale s, zero_loss_scale* __restrict__ ls)
@@ -948,16 +949,18 @@ hipError_t launch_finalize(const Partial* parts, int64_t nparts, double external
 }
 
 hipError_t launch_bucket_finalize(const PlanHeader* hdr, uint64_t sig, const zero_bucket_partial* parts, int32_t nb,
-                                  uint64_t stamp, float scale, double external, double max_norm, int skip,
-                                  zero_result* res, hipStream_t s)
+                                  uint64_t stamp, float scale, const zero_loss_scale* ls, double external,
+                                  double max_norm, int skip, zero_result* res, hipStream_t s)
 {
-    bucket_finalize_kernel<<<1, kThreads, 0, s>>>(hdr, sig, parts, nb, stamp, scale, external, max_norm, skip, res);
+    bucket_finalize_kernel<<<1, kThreads, 0, s>>>(hdr, sig, parts, nb, stamp, scale, ls, external, max_norm, skip,
+                                                  res);
     return hipGetLastError();
 }
 
-hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale, hipStream_t s)
+hipError_t launch_bucket_partial_empty(zero_bucket_partial* slot, uint64_t stamp, float scale,
+                                       const zero_loss_scale* ls, hipStream_t s)
 {
-    bucket_partial_empty_kernel<<<1, 64, 0, s>>>(slot, stamp, scale);
+    bucket_partial_empty_kernel<<<1, 64, 0, s>>>(slot, stamp, scale, ls);
     return hipGetLastError();
 }
 

@@ -324,3 +324,29 @@ def test_offload_step_argument_checks():
     assert call(a=arr3) == 1                                   # no host state
     neg, k4 = _offload(n=-1)
     assert L.zero_offload_workspace_bytes(neg, 1, 2) == 0 and L.zero_offload_host_workspace_bytes(neg, 1) == 0
+
+
+def test_amp_forms_need_their_loss_scale():
+    L = z.lib()
+    c = z.LossScaleConfig()._c()
+    bad = z.LossScaleConfig(window=0)._c()
+    h = _hp()
+    ls, res, ws, parts = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21), 1 << 24, ctypes.c_void_p(1 << 22)
+    arr, keep = _shards()
+    need = L.zero_bucket_reduce_workspace_bytes(arr, 1, 2)
+    assert L.zero_bucket_reduce_amp(arr, 1, 2, z.BUCKET_FINAL, 1.0, None, 0, parts, ws, need, None) == 1
+    acc = (z._CAccTensor * 1)()
+    acc[0] = z._CAccTensor(100, 256, 1024, 2048, 4096, 8192)
+    an = L.zero_step_accumulated_workspace_bytes(acc, 1)
+    assert L.zero_step_accumulated_amp(acc, 1, ctypes.byref(h), ctypes.byref(c), None, parts, 1, 0, 0.0, ws, an, res,
+                                       None) == 1
+    assert L.zero_step_accumulated_amp(acc, 1, ctypes.byref(h), ctypes.byref(bad), ls, parts, 1, 0, 0.0, ws, an, res,
+                                       None) == 1
+    off, k2 = _offload()
+    on = L.zero_offload_workspace_bytes(off, 1, 2)
+    hn = L.zero_offload_host_workspace_bytes(off, 1)
+    r = z._CResult()
+    assert L.zero_offload_step_amp(off, 1, 2, ctypes.byref(h), ctypes.byref(c), None, 0.0, ws, on, 1 << 25, hn,
+                                   ctypes.byref(r), 0, None) == 1
+    assert L.zero_offload_step_amp(off, 1, 2, ctypes.byref(h), None, ls, 0.0, ws, on, 1 << 25, hn, ctypes.byref(r),
+                                   0, None) == 1

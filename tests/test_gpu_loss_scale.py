@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import sharded_optimizer_step_amd as z
-from cases import Case, assert_tensor_matches, build, hp_oracle
+from cases import Case, assert_state_matches, assert_tensor_matches, build, hp_oracle, to_np_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +165,98 @@ def test_amp_step_equals_reduce_check_update_composition():
     for a, b in ((d1[0].master, d2[0].master), (d1[0].exp_avg, d2[0].exp_avg), (d1[0].exp_avg_sq, d2[0].exp_avg_sq)):
         assert torch.equal(a, b)
     assert torch.equal(d1[0].param_out.view(torch.int16), d2[0].param_out.view(torch.int16))
+
+
+def _run_plan(sizes, M):
+    """Overflows planted on chosen steps: the second in a row halves the scale,
+    every `window` clean steps double it."""
+    return {2: [(0, M - 1, 7)], 3: [(0, 0, 5)], 6: [(len(sizes) - 1, 1 % M, sizes[-1] - 1)]}
+
+
+@pytest.mark.parametrize("max_norm", [0.0, 5.0])
+def test_zero2_amp_run_matches_the_oracle(max_norm):
+    # the ZeRO-2 streaming step under the dynamic scale: bucket reduces read
+    # inv_scale on the device, the step checks the partials' multiplier,
+    # updates, then moves the scale
+    sizes, M = [100_003, 512, 4099], 4
+    case = Case(sizes, M, seed=33, grad_std=4.0)
+    dts, hts = build(case)
+    zc, oc = _cfg_pair(initial_scale_power=12, window=3, hysteresis=2, min_scale=1.0)
+    ls = z.new_loss_scale()
+    z.zero_loss_scale_init(zc, ls)
+    ref = oracle.loss_scale_init(oc)
+    buckets = [[2, 1], [0]]
+    parts = z.new_bucket_partials(len(buckets))
+    accs = [torch.empty(n, dtype=torch.float32, device="cuda") for n in sizes]
+    reducers = [z.BucketReducer([z.GradShard(dts[t].grads, accs[t]) for t in idx], parts[32 * b:32 * b + 32], ls=ls)
+                for b, idx in enumerate(buckets)]
+    ats = [z.AccTensor(a, d.master, d.exp_avg, d.exp_avg_sq, d.param_out) for a, d in zip(accs, dts)]
+    sws = z.workspace(z.zero_step_accumulated_workspace_bytes(ats))
+    res = z.new_result()
+    state = hts
+    plan = _run_plan(sizes, M)
+    t = 1
+    seen = set()
+    for k in range(10):
+        where = plan.get(k, [])
+        old = _inject(dts, state, where)
+        hp = z.HParams(step=t, max_grad_norm=max_norm)
+        for rd in reducers:
+            rd.reduce(z.BUCKET_FINAL, hp.grad_scale, 100 + k)
+        z.zero_step_accumulated_amp(ats, hp, zc, ls, parts, len(buckets), 100 + k, 0.0, sws, res)
+        r = z.read_result(res)
+        acc_h = [oracle.grad_accumulate(s_.grads) for s_ in state]
+        new, ro, ref = oracle.zero_step_accumulated_amp(acc_h, state, hp_oracle(hp), oc, ref)
+        # the step from accumulators returns no replicas: keep this run's
+        state = [oracle.TensorState(s_.grads, n_.master, n_.exp_avg, n_.exp_avg_sq, n_.param_out)
+                 for s_, n_ in zip(state, new)]
+        assert r["status"] == 0
+        assert (r["found_inf"], r["skipped"]) == (ro.found_inf, ro.skipped) == (int(bool(where)),) * 2, k
+        if not where:
+            assert math.isclose(r["sumsq"], ro.sumsq, rel_tol=1e-9), (k, r, ro)
+            t += 1
+        _same_state(z.read_loss_scale(ls), ref, f"step {k}")
+        seen.add(ref.scale)
+        for d, h in zip(dts, state):
+            assert_tensor_matches(d, h, f"step {k}")
+        _restore(dts, state, where, old)
+    assert seen == {2048.0, 4096.0}  # halved on the second overflow in a row, doubled after 3 clean steps
+
+
+def test_offload_amp_run_matches_the_oracle():
+    # the CPU-offloaded step under the dynamic scale: the GPU's fold reads and
+    # moves it, the host update is unchanged
+    sizes, M = [100_003, 4099], 4
+    case = Case(sizes, M, seed=35, grad_std=4.0)
+    dts, hts = build(case)
+    ots = [z.OffloadTensor(d.grads, torch.from_numpy(h.master.copy()), torch.from_numpy(h.exp_avg.copy()),
+                           torch.from_numpy(h.exp_avg_sq.copy()), d.param_out) for d, h in zip(dts, hts)]
+    zc, oc = _cfg_pair(initial_scale_power=12, window=3, hysteresis=2, min_scale=1.0)
+    ls = z.new_loss_scale()
+    z.zero_loss_scale_init(zc, ls)
+    ref = oracle.loss_scale_init(oc)
+    ws = z.workspace(z.zero_offload_workspace_bytes(ots, M))
+    hws = z.host_workspace(z.zero_offload_host_workspace_bytes(ots))
+    state = hts
+    plan = _run_plan(sizes, M)
+    t = 1
+    seen = set()
+    for k in range(10):
+        where = plan.get(k, [])
+        old = _inject(dts, state, where)
+        hp = z.HParams(step=t, max_grad_norm=5.0)
+        r = z.zero_offload_step_amp(ots, hp, zc, ls, 0.0, ws, hws, 3)
+        torch.cuda.synchronize()
+        state, ro, ref = oracle.zero_step_amp(state, hp_oracle(hp), oc, ref)
+        assert r["status"] == 0
+        assert (r["found_inf"], r["skipped"]) == (ro.found_inf, ro.skipped) == (int(bool(where)),) * 2, k
+        if not where:
+            assert math.isclose(r["sumsq"], ro.sumsq, rel_tol=1e-9), (k, r, ro)
+            t += 1
+        _same_state(z.read_loss_scale(ls), ref, f"step {k}")
+        seen.add(ref.scale)
+        for o, h in zip(ots, state):
+            assert_state_matches(o.master.numpy(), o.exp_avg.numpy(), o.exp_avg_sq.numpy(), to_np_u16(o.param_out),
+                                 h.master, h.exp_avg, h.exp_avg_sq, h.param_out, f"step {k}")
+        _restore(dts, state, where, old)
+    assert seen == {2048.0, 4096.0}  # halved on the second overflow in a row, doubled after 3 clean steps

@@ -193,3 +193,24 @@ def test_zero2_memory_accounting():
     z0, z1, z2, z3 = (oracle.bytes_per_gpu(P, N, s) for s in range(4))
     assert z2 == P * (2 + (2 + 12) / N)
     assert z3 < z2 < z1 < z0
+
+
+@pytest.mark.parametrize("flag_inf", [False, True])
+def test_amp_one_micro_batch_equals_the_zero1_amp_step(flag_inf):
+    # the dynamic loss scale over the accumulated gradient: with one
+    # micro-batch, state, record and the moved scale equal the ZeRO-1 AMP step's
+    rng = np.random.default_rng(25)
+    ts = _tensors([700, 33], 3, rng, std=4.0)
+    if flag_inf:
+        ts[1].grads[2][30] = 0x7F80
+    cfg = oracle.LossScaleConfig(initial_scale_power=12, window=1, hysteresis=1)
+    ls = oracle.loss_scale_init(cfg)
+    hp = oracle.HParams(step=9, max_grad_norm=3.0)
+    want, rw, lw = oracle.zero_step_amp(ts, hp, cfg, ls)
+    accs = [oracle.grad_accumulate(t.grads) for t in ts]
+    got, rg, lg = oracle.zero_step_accumulated_amp(accs, ts, hp, cfg, ls)
+    assert (rg.sumsq == rw.sumsq or flag_inf) and (rg.found_inf, rg.skipped) == (rw.found_inf, rw.skipped)
+    assert (rg.found_inf, rg.skipped) == (int(flag_inf),) * 2
+    assert lg == lw and lw.scale == (2048.0 if flag_inf else 8192.0)
+    for a, b in zip(got, want):
+        assert _same_state(a, b)
