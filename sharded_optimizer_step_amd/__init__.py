@@ -1,10 +1,12 @@
-"""Fused per-rank ZeRO-1 shard step for MI355X (gfx950): a thin ctypes binding
+"""The per-rank ZeRO shard step for MI355X (gfx950): a thin ctypes binding
 of the C ABI declared in ``include/zero_step.h``.
 
-This module only marshals arguments (torch tensors -> device pointers and the
-current HIP stream). Every step of the computation runs in the HIP kernels of
-``libzero_step.so``; there is no CPU fallback: if the library is missing the
-first call raises.
+This module only marshals arguments (torch tensors -> device or host
+pointers and the current HIP stream). Every step of the computation runs in
+``libzero_step.so``: its HIP kernels, and for the CPU-offloaded step (whose
+optimizer state lives in host memory by design) the host optimizer built
+into the same library. There is no CPU fallback: if the library is missing
+the first call raises.
 
 Functions keep the C names:
 
@@ -19,10 +21,13 @@ Functions keep the C names:
 * ``zero_bucket_reduce_workspace_bytes(shards, M)``,
   ``zero_bucket_reduce(shards, flags, grad_scale, stamp, partial, ws)``
 * ``zero_step_accumulated_workspace_bytes(tensors)``,
-  ``zero_step_accumulated(tensors, hp, partials, stamp, external_sumsq, ws, res)``
+  ``zero_step_accumulated(tensors, hp, partials, nbuckets, stamp, external_sumsq, ws, res)``,
+  ``BucketReducer(shards, partial, ws=None, ls=None).reduce(flags, grad_scale, stamp)``
 * ``zero_offload_workspace_bytes(tensors, M)``, ``zero_offload_host_workspace_bytes(tensors)``,
   ``zero_offload_step(tensors, hp, external_sumsq, ws, host_ws, threads)``,
   ``zero_offload_adamw_host(master, exp_avg, exp_avg_sq, g, param_out, hp, clip_coef, threads)``
+* ``zero_bucket_reduce_amp``, ``zero_step_accumulated_amp``, ``zero_offload_step_amp``: the same under the
+  dynamic loss scale
 * ``zero_workspace_forget(ws)``, ``zero_status_string(status)``
 """
 from __future__ import annotations

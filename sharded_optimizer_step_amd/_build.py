@@ -1,5 +1,6 @@
-"""Build the gfx950 HIP library of the fused ZeRO-1 shard step in-tree
-(hipcc cross-compiles without a GPU)."""
+"""Build the library of the per-rank ZeRO shard step in-tree: the gfx950 HIP
+kernels and the C ABI with hipcc (it cross-compiles without a GPU), the host
+optimizer of the CPU-offloaded step with g++."""
 from __future__ import annotations
 
 import os

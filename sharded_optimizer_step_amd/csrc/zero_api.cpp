@@ -1,6 +1,9 @@
-// zero_api.cpp -- the C ABI of the fused ZeRO-1 shard step: argument checks,
-// host-side scalar derivation, element layouts, the zero_step workspace plan
-// and the launch sequence. Every kernel is in zero_kernels.hip.
+// zero_api.cpp -- the C ABI of the per-rank ZeRO shard step in all its forms
+// (fused ZeRO-1, composed, ZeRO-2 streaming, CPU-offloaded, and their
+// dynamic-loss-scale variants): argument checks, host-side scalar
+// derivation, element layouts, the workspace plans and the launch sequences.
+// Every GPU kernel is in zero_kernels.hip; the host optimizer of the
+// CPU-offloaded step is in zero_host_adamw.cpp.
 #include <hip/hip_runtime.h>
 
 #include <cmath>

@@ -1,5 +1,5 @@
 // zero_internal.h -- types shared by the host library and the gfx950 kernels
-// of the fused ZeRO-1 shard step. Not part of the public C ABI.
+// of the per-rank ZeRO shard step. Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

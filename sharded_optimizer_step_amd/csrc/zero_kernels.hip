@@ -1,4 +1,4 @@
-// zero_kernels.hip -- gfx950 kernels of the fused ZeRO-1 shard step.
+// zero_kernels.hip -- gfx950 kernels of the per-rank ZeRO shard step.
 //
 // The step ("CS336 Lecture 7: Parallelism 1", section "ZeRO Stage 1", steps
 // 2-4): the M bf16 gradient replicas of this rank's shard are summed in fp32
@@ -6,6 +6,13 @@
 // into the global norm; AdamW then updates the fp32 master, m and v of the
 // shard (the 12 optimizer bytes of the table in section "训练内存的详细分析")
 // and the new master is rounded to the bf16 shard an all-gather would send.
+// The same tile loop serves the step's other forms: ZeRO-2 streaming (section
+// "ZeRO Stage 2"; Mode::Acc folds each bucket into the caller's fp32 shard
+// accumulator, its final pass emitting the bucket's norm partial, and
+// Mode::PassB then updates from the accumulator), the CPU-offloaded step
+// (Mode::PassA alone, on the GPU's side of it) and the dynamic loss scale
+// (the multiplier read from device memory, the scale moved by the fold's
+// last workgroup).
 //
 // This is streaming, HBM-bound work with no contraction, so there is no MFMA
 // here. Design points for CDNA4:
