@@ -45,7 +45,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed: a
+    profile stays valid across comment edits and goes stale on any change of
+    the code itself."""
+    import re
+    src = open(KERNEL_SRC, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+    src = re.sub(r"//[^\n]*", " ", src)                  # line comments (the source has no '//' in strings)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def parse():
