@@ -15,7 +15,7 @@ import sharded_optimizer_step_amd as z
 import synth
 from cases import (Stats, assert_state_matches, hp_oracle, host_inputs_at, oracle_sumsq_streaming, sample_indices,
                    to_np_f32, to_np_u16)
-from synth.workloads import workload
+from synth.workloads import workload, zero2_buckets
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +131,67 @@ def test_amp_workload_skip_then_clean_step():
     st = Stats()
     _check_sampled(w, tensors, hp, ro.clip_coef, [idx], st)
     print(w.name, "norm", r["grad_norm"], ro.grad_norm, "coef", r["clip_coef"], ro.clip_coef, st)
+
+
+def test_offloaded_step_on_the_7p5b_shard():
+    # the state of the 117,187,500-parameter shard moved to host memory: the
+    # offloaded step must give exactly what the fused step gives on the same
+    # replicas, and match the oracle on sampled elements
+    w = workload(2)
+    tensors = bench.build_workload(w, 0)
+    d = tensors[0]
+    spec = w.tensors[0]
+    hp = _hp(w)
+    ot = z.OffloadTensor(d.grads, d.master.cpu(), d.exp_avg.cpu(), d.exp_avg_sq.cpu(),
+                         torch.empty_like(d.param_out))
+    r_off = z.zero_offload_step([ot], hp, 0.0, z.workspace(z.zero_offload_workspace_bytes([ot], w.M)),
+                                z.host_workspace(z.zero_offload_host_workspace_bytes([ot])))
+    torch.cuda.synchronize()
+    r = _step(w, tensors, hp)
+    assert r_off["status"] == r["status"] == 0 and r_off["skipped"] == r["skipped"] == 0
+    assert math.isclose(r_off["sumsq"], r["sumsq"], rel_tol=1e-12)
+    for name in ("master", "exp_avg", "exp_avg_sq"):
+        assert torch.equal(getattr(ot, name), getattr(d, name).cpu()), name
+    assert torch.equal(ot.param_out.view(torch.int16), d.param_out.view(torch.int16))
+    idx = sample_indices(spec.n, np.random.default_rng(22), 40_000)
+    st = Stats()
+    _check_sampled(w, tensors, hp, 1.0, [idx], st)
+    print(w.name, "offloaded", st)
+
+
+def test_zero2_two_micro_batches_on_the_llama_list():
+    # the same replicas delivered twice: every accumulator holds fold + fold,
+    # checked against the oracle's two-micro-batch accumulation on sampled
+    # elements, then the step from it
+    w = workload(3)
+    tensors = bench.build_workload(w, 0)
+    buckets = zero2_buckets(w)
+    accs = [torch.empty(spec.n, dtype=torch.float32, device="cuda") for spec in w.tensors]
+    parts = z.new_bucket_partials(len(buckets))
+    hp = _hp(w)
+    reducers = [z.BucketReducer([z.GradShard(tensors[t].grads, accs[t]) for t in idx], parts[32 * b:32 * b + 32])
+                for b, idx in enumerate(buckets)]
+    for k in range(2):
+        for rd in reducers:
+            rd.reduce((z.BUCKET_ACCUMULATE if k else 0) | (z.BUCKET_FINAL if k else 0), hp.grad_scale, 9)
+    ats = [z.AccTensor(a, t.master, t.exp_avg, t.exp_avg_sq, t.param_out) for a, t in zip(accs, tensors)]
+    res = z.new_result()
+    z.zero_step_accumulated(ats, hp, parts, len(buckets), 9, 0.0,
+                            z.workspace(z.zero_step_accumulated_workspace_bytes(ats)), res)
+    r = z.read_result(res)
+    assert r["status"] == 0 and r["found_inf"] == 0 and r["skipped"] == 0
+    rng = np.random.default_rng(34)
+    st = Stats()
+    for spec, dt, acc in zip(w.tensors, tensors, accs):
+        idx = sample_indices(spec.n, rng, 200)
+        grads, master, m, v = host_inputs_at(w, spec, idx)
+        a = oracle.grad_accumulate(grads, oracle.grad_accumulate(grads))
+        sel = torch.from_numpy(idx).cuda()
+        got = acc[sel].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), a.view(np.uint32)), spec.name
+        new, _ = oracle.zero_step_accumulated([a], [oracle.TensorState([], master, m, v, None)], hp_oracle(hp))
+        h = new[0]
+        assert_state_matches(to_np_f32(dt.master[sel]), to_np_f32(dt.exp_avg[sel]), to_np_f32(dt.exp_avg_sq[sel]),
+                             to_np_u16(dt.param_out[sel]), h.master, h.exp_avg, h.exp_avg_sq, h.param_out, spec.name,
+                             st)
+    print(w.name, "ZeRO-2, 2 micro-batches", st)
