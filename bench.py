@@ -326,7 +326,7 @@ def offload_line(a, w, tensors) -> dict:
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+        print(f"bench.py: the step runs on one GPU (asked for --gpus {a.gpus}); "
               "the multi-GPU layout is a design, not a measured path", file=sys.stderr)
         sys.exit(2)
     import torch

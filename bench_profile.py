@@ -2,10 +2,10 @@
 HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter passes (one
 counter per run), calibrated on a plain device copy of known size.
 
-    python bench_profile.py --workload 2 [--steps 10] [--out gpurun_out/prof]
+    python bench_profile.py --workload 2 [--steps 10] [--out rocprof_raw]
     python bench_profile.py --zero2 [--workload 3]     (the ZeRO-2 streaming leg of bench.py)
 
-Runs on a GPU machine. Writes:
+Needs an MI355X with rocprofv3. Writes:
   profiles/<kernel>_<workload tag>.md   the figures used and the commands that made them
   profiles/traffic.json                 HBM bytes per launch of the dominant kernel, keyed by
                                         workload and the hash of the kernel source (bench.py
@@ -62,7 +62,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--out", default=os.path.join("gpurun_out", "prof"), help="raw rocprofv3 output (relative)")
+    ap.add_argument("--out", default="rocprof_raw", help="raw rocprofv3 output (relative; not committed)")
     ap.add_argument("--profiles-dir", default="profiles", help="where the summaries go (relative)")
     ap.add_argument("--summarize-only", action="store_true", help="re-read existing raw output, run nothing")
     ap.add_argument("--zero2", action="store_true", help="profile bench.py --zero2 (one micro-batch)")
