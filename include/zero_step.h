@@ -136,9 +136,10 @@ size_t zero_grad_check_norm_workspace_bytes(int64_t n);
  * zero_grad_check_norm -- non-finite check, global L2 norm, clip coefficient
  * and skip decision over an fp32 gradient g (device, n elements), written to
  * the device record res_dev. hp may be NULL (no clipping, no skip); only its
- * max_grad_norm and skip_on_nonfinite are read. external_sumsq (>= 0 or NaN/inf
- * propagates) is the other ranks' sum of squares for a multi-GPU caller; 0 on
- * one GPU. ws: device workspace of at least
+ * max_grad_norm and skip_on_nonfinite are read. external_sumsq is the other
+ * ranks' sum of squares for a multi-GPU caller, 0 on one GPU: NaN and +inf
+ * propagate into the norm, a negative value is ZERO_ERR_INVALID_ARGUMENT (as
+ * in every call that takes it). ws: device workspace of at least
  * zero_grad_check_norm_workspace_bytes(n) bytes, contents irrelevant on entry.
  * The sum of squares uses exact binary64 squares and a fixed reduction tree
  * (bitwise repeatable on one device).
@@ -175,8 +176,8 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
  * aligned. The workspace caches the tensor table of the call; it belongs to
  * the library from this call until the caller reuses it for anything else,
  * and two calls that share a workspace must not run concurrently. res_dev:
- * device result record. Returns ZERO_ERR_WORKSPACE_TOO_SMALL if ws_bytes is
- * short.
+ * device result record. external_sumsq as for zero_grad_check_norm. Returns
+ * ZERO_ERR_WORKSPACE_TOO_SMALL if ws_bytes is short.
  */
 int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
               double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
@@ -434,10 +435,12 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
  * CPU affinity mask). The call waits for the GPU's fold and returns once
  * master, m and v are updated on the host (or the step is skipped); the
  * bf16 copies into param_out are then enqueued, and `stream` is made to wait
- * for them, so work later on `stream` sees the new shard. Calls that share a
- * host workspace must be issued on one stream. Argument errors are reported
- * before anything is launched; a HIP error during the transfers
- * (ZERO_ERR_HIP) can leave the host state partly updated.
+ * for them, so work later on `stream` sees the new shard. Those copies read
+ * host_ws: it stays allocated and untouched until `stream` has passed them,
+ * and calls that share a host workspace must be issued on one stream.
+ * Argument errors are reported before anything is launched; a HIP error
+ * during the transfers (ZERO_ERR_HIP) can leave the host state partly
+ * updated, and the call drains its copies before returning it.
  */
 int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
                       double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,

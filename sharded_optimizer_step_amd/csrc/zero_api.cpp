@@ -27,6 +27,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool is_fin(double x) { return std::isfinite(x); }
 
+// The other ranks' sum of squares: NaN and +inf pass into the norm (a rank
+// saw a non-finite gradient); a negative value is no sum of squares.
+bool external_ok(double x) { return !(x < 0.0); }
+
 bool hparams_ok(const zero_adamw_hparams* hp)
 {
     if (hp == nullptr) return false;
@@ -361,7 +365,8 @@ int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
               const zero_loss_scale_config* lscfg, zero_loss_scale* ls)
 {
     // ---- arguments
-    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr)
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr ||
+        !external_ok(external_sumsq))
         return ZERO_ERR_INVALID_ARGUMENT;
     if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     int64_t total_n = 0;
@@ -468,7 +473,7 @@ size_t zero_grad_check_norm_workspace_bytes(int64_t n)
 int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp, double external_sumsq, void* ws,
                          size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
 {
-    if (n < 0 || res_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    if (n < 0 || res_dev == nullptr || !external_ok(external_sumsq)) return ZERO_ERR_INVALID_ARGUMENT;
     if (hp != nullptr && !hparams_ok(hp)) return ZERO_ERR_INVALID_ARGUMENT;
     const double max_norm = hp ? hp->max_grad_norm : 0.0;
     const int skip = hp ? (hp->skip_on_nonfinite != 0) : 0;
@@ -652,7 +657,8 @@ static int acc_step_impl(const zero_acc_tensor* tensors, int32_t T, const zero_a
                          const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
                          double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
 {
-    if (!acc_tensors_ok(tensors, T) || !hparams_ok(hp) || res_dev == nullptr || nbuckets < 0)
+    if (!acc_tensors_ok(tensors, T) || !hparams_ok(hp) || res_dev == nullptr || nbuckets < 0 ||
+        !external_ok(external_sumsq))
         return ZERO_ERR_INVALID_ARGUMENT;
     if (nbuckets > 0 && partials_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     int64_t total_n = 0;
@@ -846,7 +852,8 @@ static int offload_impl(const zero_offload_tensor* tensors, int32_t T, int32_t M
                         int32_t threads, hipStream_t stream)
 {
     // ---- arguments (nothing is launched on an error)
-    if (!offload_tensors_ok(tensors, T, M) || !hparams_ok(hp) || res_host == nullptr || threads < 0)
+    if (!offload_tensors_ok(tensors, T, M) || !hparams_ok(hp) || res_host == nullptr || threads < 0 ||
+        !external_ok(external_sumsq))
         return ZERO_ERR_INVALID_ARGUMENT;
     std::vector<PlanTensor> pts(static_cast<size_t>(T));
     int64_t total_n = 0;
@@ -953,6 +960,11 @@ static int offload_impl(const zero_offload_tensor* tensors, int32_t T, int32_t M
             if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess ||
                 hipEventRecord(done, up) != hipSuccess || hipStreamWaitEvent(stream, done, 0) != hipSuccess)
                 status = ZERO_ERR_HIP;
+        }
+        if (status != ZERO_OK) {
+            // no copy into or out of host_ws may outlive a failed call
+            (void)hipStreamSynchronize(stream);
+            (void)hipStreamSynchronize(up);
         }
         if (done != nullptr) (void)hipEventDestroy(done);
         for (size_t i = 0; i < made; ++i) (void)hipEventDestroy(chunks[i].ready);

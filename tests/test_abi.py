@@ -169,6 +169,46 @@ def test_zero_step_argument_checks():
     assert L.zero_step_workspace_bytes(arr3, 1, 2, ctypes.byref(h)) == 0
 
 
+@pytest.mark.parametrize("ext", [-1.0, -1e-300, float("-inf")])
+def test_negative_external_sumsq_is_rejected_without_launch(ext):
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(100, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    res = ctypes.c_void_p(1 << 20)
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), ext, 1 << 24, need, res, None) == 1
+    assert L.zero_step(arr, 0, 2, ctypes.byref(h), ext, 1 << 24, need, res, None) == 1     # empty list too
+    cfg = z.LossScaleConfig()._c()
+    assert L.zero_step_amp(arr, 1, 2, ctypes.byref(h), ctypes.byref(cfg), ctypes.c_void_p(1 << 22), ext, 1 << 24,
+                           need, res, None) == 1
+    assert L.zero_grad_check_norm(256, 10, None, ext, 1024, 1 << 20, 512, None) == 1
+    assert L.zero_grad_check_norm(None, 0, None, ext, None, 0, 512, None) == 1
+    acc = (z._CAccTensor * 1)()
+    acc[0] = z._CAccTensor(100, 256, 1024, 2048, 4096, 8192)
+    aneed = L.zero_step_accumulated_workspace_bytes(acc, 1)
+    assert L.zero_step_accumulated(acc, 1, ctypes.byref(h), ctypes.c_void_p(1 << 21), 1, 0, ext, 1 << 24, aneed,
+                                   res, None) == 1
+    off, keep = _offload()
+    r = z._CResult()
+    assert L.zero_offload_step(off, 1, 2, ctypes.byref(h), ext, 1 << 24, L.zero_offload_workspace_bytes(off, 1, 2),
+                               1 << 25, L.zero_offload_host_workspace_bytes(off, 1), ctypes.byref(r), 0, None) == 1
+
+
+@pytest.mark.parametrize("ext", [float("nan"), float("inf"), 0.0, 2.5])
+def test_nonnegative_or_nonfinite_external_sumsq_passes_the_checks(ext):
+    # NaN and +inf carry another rank's non-finite gradient into the norm: the
+    # call gets as far as the workspace check
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(100, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), ext, 1 << 24, need - 1, ctypes.c_void_p(1 << 20), None) == 2
+
+
 def test_workspace_sizes_follow_the_traffic_plan():
     one = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams())
     two = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams(max_grad_norm=1.0))
