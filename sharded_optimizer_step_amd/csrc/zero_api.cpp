@@ -115,12 +115,17 @@ int64_t tiles_of(const std::vector<Layout>& layouts, int geom)
 // workgroup lockstep -- for a single pass 512 threads x 16 vectors (128 KiB of
 // one replica per workgroup, registers to spare for the binary64 update) when
 // the replica reads dominate (M > 16), else 256 x 16, whose two workgroups
-// per CU overlap one's state update with the other's fold; 1024 x 8 for the
-// first pass of a two-pass step (no update, more waves) -- unless the bucket
-// is too small to reach half the compute units.
+// per CU overlap one's state update with the other's fold; for a first pass
+// that only folds (two-pass step, bucket reduce, offloaded fold), 512 x 16
+// from four tiles per CU on, below that 1024 x 8 (more waves per tile) --
+// unless the bucket is too small to reach half the compute units.
 int pick_geom_fold(const std::vector<Layout>& layouts, int M, bool two_pass, int cus)
 {
-    const int first = two_pass ? 4 : (M > 16 ? 5 : 6);
+    int first;
+    if (!two_pass)
+        first = M > 16 ? 5 : 6;
+    else
+        first = tiles_of(layouts, 5) >= 4 * static_cast<int64_t>(cus) ? 5 : 4;
     if (2 * tiles_of(layouts, first) >= static_cast<int64_t>(cus)) return first;
     for (int g = 3; g > 0; --g)
         if (2 * tiles_of(layouts, g) >= static_cast<int64_t>(cus)) return g;

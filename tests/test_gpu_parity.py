@@ -225,6 +225,24 @@ def test_zero_step_two_pass(max_norm, skip, scale):
         assert ro.clip_coef < 1.0
 
 
+def test_zero_step_two_pass_with_many_tiles_per_cu():
+    # 67M elements: the first pass has over four 65536-element tiles per CU,
+    # where it switches to its long-burst geometry; every element checked
+    M = 3
+    case = Case([1024 * 65536 + 12_345, 4099], M, seed=61, grad_std=1e-4)
+    dts, hts = build(case)
+    hp = z.HParams(step=100, max_grad_norm=0.5, skip_on_nonfinite=1)
+    r, _ = run_step(dts, hp)
+    new, ro = oracle.zero_step(hts, hp_oracle(hp))
+    st = Stats()
+    for i, (d, h) in enumerate(zip(dts, new)):
+        assert_tensor_matches(d, h, f"tensor {i}", st)
+    assert r["found_inf"] == 0 and r["skipped"] == 0 and ro.clip_coef < 1.0
+    assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
+    assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-6 * ro.clip_coef
+    print(st)
+
+
 def test_zero_step_ragged_unaligned_bucket():
     sizes = [512, 0, 1, 7, 8, 4099, 11_011, 4097, 2048, 2047, 2049, 300_001]
     M = 4
