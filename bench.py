@@ -406,7 +406,8 @@ def main():
         tf = json.load(open(TRAFFIC_FILE))
         ent = tf.get(str(a.workload))
         if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp:
-            traffic = ent["bytes_per_launch"]
+            # the one fused launch of a single-pass step; both launches of a two-pass step
+            traffic = ent["bytes_per_launch"] if not w.two_pass else ent.get("bytes_per_step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     cpu = None

@@ -7,9 +7,10 @@ counter per run), calibrated on a plain device copy of known size.
 
 Needs an MI355X with rocprofv3. Writes:
   profiles/<kernel>_<workload tag>.md   the figures used and the commands that made them
-  profiles/traffic.json                 HBM bytes per launch of the dominant kernel, keyed by
-                                        workload and the hash of the kernel source (bench.py
-                                        reports it only while that hash is current)
+  profiles/traffic.json                 HBM bytes per launch of the dominant kernel and per
+                                        step (every launch of the step), keyed by workload and
+                                        the hash of the kernel source (bench.py reports it only
+                                        while that hash is current)
 Raw rocprofv3 output stays under --out.
 """
 from __future__ import annotations
@@ -109,6 +110,14 @@ def main():
     fetch_b = fetch_kib * 1024 / f_fetch
     write_b = write_kib * 1024 / f_write
     n = w.n_total
+    # every fused launch of the timed command, per step (the dominant kernel
+    # runs once per step): both passes of a two-pass step
+    is_fused = lambda name: "fused_kernel" in name
+    fetch_rows = list(csv.DictReader(open(one(f"{out}/fetch/run_counter_collection.csv"))))
+    write_rows = list(csv.DictReader(open(one(f"{out}/write/run_counter_collection.csv"))))
+    step_b = (sum(float(r["Counter_Value"]) for r in fetch_rows if is_fused(r["Kernel_Name"])) / nf * 1024 / f_fetch
+              + sum(float(r["Counter_Value"]) for r in write_rows if is_fused(r["Kernel_Name"])) / nw * 1024 / f_write)
+    alg_step = (2 * w.M + (34 if w.two_pass else 26)) * n
     # bytes of the dominant kernel by the traffic model: single pass 2M+26, or the
     # fold pass (2M+4) / update pass (30) of a two-pass step
     if not w.two_pass:
@@ -145,11 +154,14 @@ def main():
         f.write(f"- WRITE_SIZE {write_kib:,.1f} KiB over {nw} dispatches -> {write_b:,.0f} B written\n")
         f.write(f"- traffic {fetch_b + write_b:,.0f} B per launch = {(fetch_b + write_b) / alg:.4f} x the "
                 f"algorithmic bytes\n")
+        f.write(f"- every fused launch of a step together: {step_b:,.0f} B per step = {step_b / alg_step:.4f} x "
+                f"the step's algorithmic bytes ({alg_step / n:.0f} B x {n:,})\n")
         f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
     tf_path = os.path.join(profiles, "traffic.json")
     tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
     tf[str(a.workload)] = {"kernel": kshort, "kernel_source_sha256_16": src_hash(),
                            "bytes_per_launch": round(fetch_b + write_b), "read_bytes": round(fetch_b),
+                           "bytes_per_step": round(step_b), "algorithmic_bytes_per_step": alg_step,
                            "write_bytes": round(write_b), "algorithmic_bytes": alg,
                            "rocprof_avg_us": round(avg_us, 2), "fetch_factor": round(f_fetch, 5),
                            "write_factor": round(f_write, 5), "summary": os.path.join("profiles", os.path.basename(md))}
