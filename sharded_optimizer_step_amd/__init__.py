@@ -231,6 +231,21 @@ def _need(t: torch.Tensor, dtype, name: str, n: Optional[int] = None):
         raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
 
 
+def _need_ws(ws: Optional[torch.Tensor], name: str = "ws") -> int:
+    """A device workspace (any dtype, contiguous) or None; returns its bytes.
+    The library writes through it from kernels: a host tensor here would be a
+    host address on the GPU."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not ws.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _check(status: int, where: str):
     if status != ZERO_OK:
         raise ZeroError(status, where)
@@ -271,7 +286,7 @@ def zero_grad_check_norm(g: torch.Tensor, hp: Optional[HParams], external_sumsq:
     _need(g, torch.float32, "g")
     _need(res, torch.uint8, "res", RESULT_BYTES)
     h = hp._c() if hp is not None else None
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_grad_check_norm(g.data_ptr(), g.numel(), ctypes.byref(h) if h is not None else None,
                                       float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
            "zero_grad_check_norm")
@@ -323,7 +338,7 @@ def zero_step(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float,
     _need(res, torch.uint8, "res", RESULT_BYTES)
     arr, keep, M = _ctensors(tensors, check=True)
     h = hp._c()
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), _ptr(ws), wsb,
                            res.data_ptr(), _stream(stream)), "zero_step")
 
@@ -380,7 +395,7 @@ def zero_step_amp(tensors: Sequence[ZeroTensor], hp: HParams, cfg: LossScaleConf
     arr, keep, M = _ctensors(tensors, check=True)
     h = hp._c()
     c = cfg._c()
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_step_amp(arr, len(tensors), M, ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
                                float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
            "zero_step_amp")
@@ -448,7 +463,7 @@ def zero_bucket_reduce(shards: Sequence[GradShard], flags: int, grad_scale: floa
     if partial is not None:
         _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
     arr, keep, M = _cshards(shards, check=True)
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_bucket_reduce(arr, len(shards), M, int(flags), float(grad_scale), int(stamp) & (2**64 - 1),
                                     _ptr(partial), _ptr(ws), wsb, _stream(stream)), "zero_bucket_reduce")
 
@@ -471,7 +486,7 @@ class BucketReducer:
             ws = workspace(zero_bucket_reduce_workspace_bytes(self._shards, self.M))
         self.ws = ws
         self._wsp = _ptr(ws)
-        self._wsb = ws.numel() * ws.element_size() if ws is not None else 0
+        self._wsb = _need_ws(ws)
         self._pp = _ptr(partial)
         if ls is not None:
             _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
@@ -495,7 +510,7 @@ def zero_bucket_reduce_amp(shards: Sequence[GradShard], flags: int, grad_scale: 
     if partial is not None:
         _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
     arr, keep, M = _cshards(shards, check=True)
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_bucket_reduce_amp(arr, len(shards), M, int(flags), float(grad_scale), ls.data_ptr(),
                                         int(stamp) & (2**64 - 1), _ptr(partial), _ptr(ws), wsb, _stream(stream)),
            "zero_bucket_reduce_amp")
@@ -529,7 +544,7 @@ def zero_step_accumulated(tensors: Sequence[AccTensor], hp: HParams, partials: O
             raise ValueError(f"partials: {partials.numel()} bytes for {nbuckets} buckets")
     arr = _cacc(tensors, check=True)
     h = hp._c()
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_step_accumulated(arr, len(tensors), ctypes.byref(h), _ptr(partials), int(nbuckets),
                                        int(stamp) & (2**64 - 1), float(external_sumsq), _ptr(ws), wsb,
                                        res.data_ptr(), _stream(stream)), "zero_step_accumulated")
@@ -603,6 +618,8 @@ def zero_offload_step(tensors: Sequence[OffloadTensor], hp: HParams, external_su
     """Returns the result record (the call reads it on the host)."""
     _need(ws, torch.uint8, "ws")
     _need_host(host_ws, torch.uint8, "host_ws")
+    if not host_ws.is_pinned():
+        raise ValueError("host_ws: must be pinned host memory (host_workspace())")
     arr, keep, M = _coffload(tensors, check=True)
     h = hp._c()
     r = _CResult()
@@ -639,7 +656,7 @@ def zero_step_accumulated_amp(tensors: Sequence[AccTensor], hp: HParams, cfg: "L
     arr = _cacc(tensors, check=True)
     h = hp._c()
     c = cfg._c()
-    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    wsb = _need_ws(ws)
     _check(lib().zero_step_accumulated_amp(arr, len(tensors), ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
                                            _ptr(partials), int(nbuckets), int(stamp) & (2**64 - 1),
                                            float(external_sumsq), _ptr(ws), wsb, res.data_ptr(), _stream(stream)),
@@ -651,6 +668,8 @@ def zero_offload_step_amp(tensors: Sequence[OffloadTensor], hp: HParams, cfg: "L
                           stream=None) -> dict:
     _need(ws, torch.uint8, "ws")
     _need_host(host_ws, torch.uint8, "host_ws")
+    if not host_ws.is_pinned():
+        raise ValueError("host_ws: must be pinned host memory (host_workspace())")
     _need(ls, torch.uint8, "ls", LOSS_SCALE_BYTES)
     arr, keep, M = _coffload(tensors, check=True)
     h = hp._c()

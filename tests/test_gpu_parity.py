@@ -397,6 +397,35 @@ def test_workspace_too_small_raises():
     assert e.value.status == z.ZERO_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_binding_rejects_host_workspaces_before_any_launch():
+    M = 2
+    case = Case([4099], M, seed=97)
+    dts, hts = build(case)
+    hp = z.HParams(step=3)
+    res = z.new_result()
+    host_ws = torch.empty(z.zero_step_workspace_bytes(dts, M, hp), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="ws: must be a device tensor"):
+        z.zero_step(dts, hp, 0.0, host_ws, res)
+    acc = torch.empty(4099, dtype=torch.float32, device="cuda")
+    sh = [z.GradShard(dts[0].grads, acc)]
+    with pytest.raises(ValueError, match="ws: must be a device tensor"):
+        z.zero_bucket_reduce(sh, z.BUCKET_FINAL, 1.0, 1, z.new_bucket_partials(1), torch.empty(4096, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="ws: must be a device tensor"):
+        z.BucketReducer(sh, z.new_bucket_partials(1), torch.empty(4096, dtype=torch.uint8))
+    ats = [z.AccTensor(acc, dts[0].master, dts[0].exp_avg, dts[0].exp_avg_sq, dts[0].param_out)]
+    with pytest.raises(ValueError, match="ws: must be a device tensor"):
+        z.zero_step_accumulated(ats, hp, z.new_bucket_partials(1), 1, 1, 0.0, torch.empty(4096, dtype=torch.uint8),
+                                res)
+    ots = [z.OffloadTensor(dts[0].grads, torch.from_numpy(hts[0].master.copy()), torch.from_numpy(hts[0].exp_avg.copy()),
+                           torch.from_numpy(hts[0].exp_avg_sq.copy()), dts[0].param_out)]
+    pageable = torch.empty(z.zero_offload_host_workspace_bytes(ots), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="pinned"):
+        z.zero_offload_step(ots, hp, 0.0, z.workspace(z.zero_offload_workspace_bytes(ots, M)), pageable)
+    torch.cuda.synchronize()
+    # nothing ran: the state is the one build() wrote
+    assert bits_equal(to_np_f32(dts[0].master), hts[0].master)
+
+
 def test_empty_bucket_writes_the_record():
     res = z.new_result()
     z.zero_step([z.ZeroTensor([torch.empty(0, dtype=torch.bfloat16, device="cuda")] * 2,
