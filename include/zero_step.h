@@ -46,6 +46,9 @@
  *    exception crosses the ABI.
  *  - Any alignment is accepted; when all pointers of a tensor share their
  *    alignment modulo 16 bytes the kernels use 16-byte vector accesses.
+ *  - The fused forms launch one workgroup per tile of a pass, at most
+ *    2^31 - 1 tiles (an update pass's tiles hold 2048 elements: about 4.4e12
+ *    elements per call); a larger call is ZERO_ERR_INVALID_ARGUMENT.
  *  - Outputs must not alias inputs, except the in-place master/exp_avg/
  *    exp_avg_sq. The library never advances `step`: the caller increments it
  *    when the result record says `skipped == 0`.

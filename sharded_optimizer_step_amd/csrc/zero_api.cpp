@@ -294,6 +294,8 @@ int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void*
         }
         for (int p = 0; p < 2; ++p) tiles[p] += d.ntiles[p];
     }
+    // one workgroup per tile: a pass launches at most 2^31 - 1 of them
+    if (tiles[0] > 0x7FFFFFFF || tiles[1] > 0x7FFFFFFF) return ZERO_ERR_INVALID_ARGUMENT;
     hdr->tiles[0] = tiles[0];
     hdr->tiles[1] = tiles[1];
     hdr->T = T;

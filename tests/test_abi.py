@@ -209,6 +209,18 @@ def test_nonnegative_or_nonfinite_external_sumsq_passes_the_checks(ext):
     assert L.zero_step(arr, 1, 2, ctypes.byref(h), ext, 1 << 24, need - 1, ctypes.c_void_p(1 << 20), None) == 2
 
 
+def test_a_pass_beyond_the_launch_limit_is_rejected_before_any_launch():
+    # 2^43 elements: the update pass would need 2^32 tiles of 2048 elements
+    L = z.lib()
+    h = _hp(max_grad_norm=1.0)
+    ptrs = (ctypes.c_void_p * 2)(256, 512)
+    arr = (z._CTensor * 1)()
+    arr[0] = z._CTensor(1 << 43, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), 1024, 2048, 4096, 8192)
+    need = L.zero_step_workspace_bytes(arr, 1, 2, ctypes.byref(h))
+    assert need > 4 << 43
+    assert L.zero_step(arr, 1, 2, ctypes.byref(h), 0.0, 1 << 24, need, ctypes.c_void_p(1 << 20), None) == 1
+
+
 def test_workspace_sizes_follow_the_traffic_plan():
     one = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams())
     two = z.zero_step_workspace_bytes_for_sizes([1_000_000], 8, z.HParams(max_grad_norm=1.0))
