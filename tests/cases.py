@@ -110,9 +110,11 @@ def assert_state_matches(got_master, got_m, got_v, got_out, want_master, want_m,
         g = got.astype(np.float64)
         w = want.astype(np.float64)
         both_nan = np.isnan(g) & np.isnan(w)
-        err = np.where(both_nan, 0.0, np.abs(g - w))
+        same = both_nan | (g == w)  # NaN in both, or equal values (infinities included)
+        with np.errstate(invalid="ignore"):
+            err = np.where(same, 0.0, np.abs(g - w))
         tol = np.maximum(2e-6 * np.abs(w), 1e-7)
-        bad = ~(err <= tol)
+        bad = ~same & ~(err <= tol)
         if bad.any():
             i = int(np.flatnonzero(bad)[0])
             raise AssertionError(f"{where} {name}[{i}]: got {got[i]!r} want {want[i]!r} "
