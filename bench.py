@@ -156,6 +156,41 @@ def cpu_baseline(w, sample: int) -> dict:
             "sample": f"first {S:,} elements of the shard with all {w.M} replicas ({dt:.1f} s, single thread)"}
 
 
+def skipped_steps(a, w, tensors, step, res, stream) -> dict:
+    """After the clean steps: the seeded +inf values of an odd run planted in
+    the replicas, K more steps timed (each must come back skipped: the fold
+    pass runs, the update pass exits), then the replicas restored."""
+    import torch
+
+    import sharded_optimizer_step_amd as z
+    import synth
+
+    spec = w.tensors[0]
+    pos = synth.inject_positions(w.seed, 1, w.M, spec.n, w.inject_rate)
+    g16 = [g.view(torch.int16) for g in tensors[0].grads]
+    saved = [(r, i, int(g16[r][i].item())) for r, i in pos]
+    for r, i in pos:
+        g16[r][i] = 0x7F80  # +inf
+    K = a.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(K):
+        step(a.warmup + K + i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    r = z.read_result(res)
+    for rr, i, v in saved:
+        g16[rr][i] = v
+    torch.cuda.synchronize()
+    if r["status"] != 0 or r["found_inf"] != 1 or r["skipped"] != 1:
+        raise RuntimeError(f"an injected step was not skipped: {r}")
+    ms = ev[0].elapsed_time(ev[1]) / K
+    n = w.n_total
+    return {"infs_planted": len(pos), "ms_per_step": round(ms, 4),
+            "hbm_gbs": round((2 * w.M + 4) * n / (ms * 1e-3) / 1e9, 1), "bytes_per_param": 2 * w.M + 4}
+
+
 def zero2_line(a, w, tensors) -> dict:
     """Times the ZeRO-2 streaming step; returns the fields of the JSON line."""
     import torch
@@ -410,6 +445,7 @@ def main():
             traffic = ent["bytes_per_launch"] if not w.two_pass else ent.get("bytes_per_step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    skipped = skipped_steps(a, w, tensors, step, res, stream) if w.inject_rate > 0 else None
     cpu = None
     if a.cpu_sample > 0:
         cpu = cpu_baseline(w, a.cpu_sample)
@@ -421,7 +457,8 @@ def main():
                    "bytes_per_param": bpp, "two_pass": w.two_pass or a.amp, "step_t": hp0["step"],
                    "loss_scale": "dynamic, on device" if a.amp else "fixed",
                    "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
-                   "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4)},
+                   "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4),
+                   **({"skipped_steps": skipped} if skipped else {})},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
