@@ -457,6 +457,9 @@ def main():
                    "bytes_per_param": bpp, "two_pass": w.two_pass or a.amp, "step_t": hp0["step"],
                    "loss_scale": "dynamic, on device" if a.amp else "fixed",
                    "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
+                   # the single-pass traffic model (2M + 26 B) over the same time, for a two-pass step
+                   **({"hbm_gbs_at_2M_plus_26": round((2 * w.M + 26) * n / (total_ms * 1e-3 / K) / 1e9, 1)}
+                      if bpp != 2 * w.M + 26 else {}),
                    "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4),
                    **({"skipped_steps": skipped} if skipped else {})},
         "roofline": roofline, "cpu_baseline": cpu,
