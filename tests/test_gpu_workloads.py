@@ -133,6 +133,62 @@ def test_amp_workload_skip_then_clean_step():
     print(w.name, "norm", r["grad_norm"], ro.grad_norm, "coef", r["clip_coef"], ro.clip_coef, st)
 
 
+def test_amp_workload_under_the_dynamic_loss_scale():
+    # the bench's --amp leg at full size: the scale held on the device starts
+    # at 1/grad_scale = 2^16 (so a clean step is the fixed-scale step), then
+    # two steps with the seeded +inf values planted are skipped and, at
+    # hysteresis 2, the second halves the scale
+    w = workload(4)
+    tensors = bench.build_workload(w, 0)
+    dt = tensors[0]
+    spec = w.tensors[0]
+    power = int(round(-math.log2(w.grad_scale)))
+    assert 2.0 ** -power == w.grad_scale
+    kw = dict(initial_scale_power=power, window=1000, hysteresis=2, min_scale=1.0)
+    cfg, ocfg = z.LossScaleConfig(**kw), oracle.LossScaleConfig(**kw)
+    hp = _hp(w)
+    hp.grad_scale = 1.0  # the multiplier comes from the device state
+    ls = z.new_loss_scale()
+    z.zero_loss_scale_init(cfg, ls)
+    ols = oracle.loss_scale_init(ocfg)
+    ws = z.workspace(z.zero_step_amp_workspace_bytes(tensors, w.M, hp))
+    res = z.new_result()
+
+    # clean step
+    z.zero_step_amp(tensors, hp, cfg, ls, 0.0, ws, res)
+    r = z.read_result(res)
+    s, f = oracle_sumsq_streaming(w)
+    ro = oracle.finalize(s, 0.0, f, hp.max_grad_norm, 1)
+    assert r["status"] == 0 and r["found_inf"] == 0 and r["skipped"] == 0
+    assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm and ro.clip_coef < 1.0
+    st = Stats()
+    _check_sampled(w, tensors, hp, ro.clip_coef, [sample_indices(spec.n, np.random.default_rng(44), 40_000)], st)
+    ols = oracle.loss_scale_update(ols, ocfg, 0)
+    assert z.read_loss_scale(ls) == dict(scale=ols.scale, inv_scale=ols.inv_scale, good_steps=ols.good_steps,
+                                         overflows=ols.overflows)
+
+    # two overflowed steps: skipped, state untouched, the second halves the scale
+    pos = synth.inject_positions(w.seed, 1, w.M, spec.n, w.inject_rate)
+    for rnk, i in pos:
+        dt.grads[rnk].view(torch.int16)[i] = 0x7F80
+    probe = np.unique(np.array([i for _, i in pos], np.int64))
+    before = [to_np_f32(_gather(x, probe)).copy() for x in (dt.master, dt.exp_avg, dt.exp_avg_sq)]
+    out_before = to_np_u16(_gather(dt.param_out, probe)).copy()
+    for k in range(2):
+        z.zero_step_amp(tensors, hp, cfg, ls, 0.0, ws, res)
+        r = z.read_result(res)
+        assert r["status"] == 0 and r["found_inf"] == 1 and r["skipped"] == 1, (k, r)
+        ols = oracle.loss_scale_update(ols, ocfg, 1)
+        got = z.read_loss_scale(ls)
+        assert got == dict(scale=ols.scale, inv_scale=ols.inv_scale, good_steps=ols.good_steps,
+                           overflows=ols.overflows), (k, got, ols)
+    assert got["scale"] == 2.0 ** (power - 1)
+    for b, x in zip(before, (dt.master, dt.exp_avg, dt.exp_avg_sq)):
+        assert np.array_equal(to_np_f32(_gather(x, probe)).view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(to_np_u16(_gather(dt.param_out, probe)), out_before)
+    print(w.name, "AMP norm", r, ro.grad_norm, st)
+
+
 def test_offloaded_step_on_the_7p5b_shard():
     # the state of the 117,187,500-parameter shard moved to host memory: the
     # offloaded step must give exactly what the fused step gives on the same
