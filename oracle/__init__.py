@@ -29,7 +29,7 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no GPU code involved)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm", "-pthread"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 

@@ -71,7 +71,10 @@
  * Compile with -O2 -ffp-contract=off and without -ffast-math: the binary32
  * fold of step 1 must be exactly the sequence of rounded adds written here.
  */
+#define _POSIX_C_SOURCE 200809L /* pthread_once */
+
 #include <math.h>
+#include <pthread.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -100,14 +103,15 @@ static float bf16_value_from_fields(uint16_t h)
 }
 
 static float g_bf16_table[65536];
-static int g_bf16_table_ready = 0;
+static pthread_once_t g_bf16_table_once = PTHREAD_ONCE_INIT;
 
-static void bf16_table_init(void)
+static void bf16_table_fill(void)
 {
-    if (g_bf16_table_ready) return;
     for (uint32_t h = 0; h < 65536u; ++h) g_bf16_table[h] = bf16_value_from_fields((uint16_t)h);
-    g_bf16_table_ready = 1;
 }
+
+/* Filled once per process, also when several threads call in at once. */
+static void bf16_table_init(void) { pthread_once(&g_bf16_table_once, bf16_table_fill); }
 
 static inline float bf16_to_float(uint16_t h) { return g_bf16_table[h]; }
 
