@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--offload", action="store_true",
                    help="the CPU-offloaded step: zero_offload_step with the optimizer state in host memory")
     p.add_argument("--threads", type=int, default=0, help="--offload: host threads (0: the CPU affinity mask)")
+    p.add_argument("--composed", action="store_true",
+                   help="the same step through the three composed entry points (zero_shard_reduce, "
+                        "zero_grad_check_norm, zero_adamw_step; single-tensor workloads)")
     p.add_argument("--amp", action="store_true",
                    help="step with zero_step_amp: the loss scale held on the device, starting at the workload's "
                         "1/grad_scale (a power of two), window 1000, hysteresis 2")
@@ -407,7 +410,19 @@ def main():
     hp = z.HParams(**hp0)
     res = z.new_result()
     stream = torch.cuda.current_stream()
-    if a.amp:
+    if a.composed:
+        if a.amp or len(tensors) != 1:
+            sys.exit("bench.py --composed: single-tensor workloads, fixed loss scale")
+        T = tensors[0]
+        g = torch.empty(T.master.numel(), dtype=torch.float32, device="cuda")
+        ws = z.workspace(z.zero_grad_check_norm_workspace_bytes(g.numel()))
+
+        def step(i):
+            hp.step = hp0["step"] + i
+            z.zero_shard_reduce(T.grads, hp.grad_scale, g, stream)
+            z.zero_grad_check_norm(g, hp, 0.0, ws, res, stream)
+            z.zero_adamw_step(T.master, T.exp_avg, T.exp_avg_sq, g, T.param_out, hp, res, stream)
+    elif a.amp:
         import math
         power = -math.log2(hp.grad_scale)
         if power != int(power):
@@ -448,17 +463,19 @@ def main():
     avg_ms = total_ms / K
     n = w.n_total
     bpp = w.bytes_per_param() if not a.amp else 2 * w.M + 34  # the AMP step is always two-pass
+    if a.composed:
+        bpp = 2 * w.M + 38  # reduce 2M + 4, check 4, update 30
     achieved = bpp * n / (avg_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
         ent = tf.get(str(a.workload))
-        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp:
+        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp and not a.composed:
             # the one fused launch of a single-pass step; both launches of a two-pass step
             traffic = ent["bytes_per_launch"] if not w.two_pass else ent.get("bytes_per_step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-    skipped = skipped_steps(a, w, tensors, step, res, stream) if w.inject_rate > 0 else None
+    skipped = skipped_steps(a, w, tensors, step, res, stream) if w.inject_rate > 0 and not a.composed else None
     cpu = None
     if a.cpu_sample > 0:
         cpu = cpu_baseline(w, a.cpu_sample)
@@ -469,6 +486,8 @@ def main():
         "config": {"workload": w.name, "shard_params": n, "M": w.M, "tensors": len(w.tensors),
                    "bytes_per_param": bpp, "two_pass": w.two_pass or a.amp, "step_t": hp0["step"],
                    "loss_scale": "dynamic, on device" if a.amp else "fixed",
+                   **({"form": "composed: zero_shard_reduce, zero_grad_check_norm, zero_adamw_step"}
+                      if a.composed else {}),
                    "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
                    # the single-pass traffic model (2M + 26 B) over the same time, for a two-pass step
                    **({"hbm_gbs_at_2M_plus_26": round((2 * w.M + 26) * n / (total_ms * 1e-3 / K) / 1e9, 1)}
