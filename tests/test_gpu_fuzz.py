@@ -67,7 +67,7 @@ def check_record(r, ro, where):
         assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-6 * ro.clip_coef, (where, r, ro)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_layouts_through_every_form(seed):
     sizes, M, offsets, hp = draw(seed)
     std = 1e-3 / hp.grad_scale
