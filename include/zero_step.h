@@ -420,7 +420,7 @@ typedef struct zero_offload_tensor {
 } zero_offload_tensor;
 
 /* Device workspace size of zero_offload_step (plan, result record, the fp32
- * gradient); 0 on invalid arguments. */
+ * gradient, one 32-byte partial per fold group); 0 on invalid arguments. */
 size_t zero_offload_workspace_bytes(const zero_offload_tensor* tensors, int32_t T, int32_t M);
 
 /* Pinned host workspace size of zero_offload_step (staging: 4 bytes of
@@ -444,6 +444,11 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
  * Argument errors are reported before anything is launched; a HIP error
  * during the transfers (ZERO_ERR_HIP) can leave the host state partly
  * updated, and the call drains its copies before returning it.
+ * Without clipping, skipping or a dynamic loss scale the update needs nothing
+ * global, so the fold runs in groups of tiles and the host updates each piece
+ * of the gradient as it arrives; the state is the same as with one fold pass
+ * (and as zero_step's), while the reported sum of squares combines the group
+ * partials in group order (it may differ from zero_step's in the last bits).
  */
 int zero_offload_step(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
                       double external_sumsq, void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,

@@ -6,6 +6,8 @@
 // CPU-offloaded step is in zero_host_adamw.cpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -206,6 +208,9 @@ struct PlanTensor {
 
 struct Plan {
     std::vector<float*> gbuf;  // per tensor: the fp32 gradient the fold pass writes (null unless kept)
+    std::vector<Layout> layouts;        // per tensor: the element layout the kernels follow
+    std::vector<int64_t> fold_begin;    // per tensor: its first tile in the fold pass's map
+    std::vector<int64_t> fold_tiles;    // per tensor: its tiles in the fold pass
     PlanOffsets off;
     int geom[2];
     int64_t tiles[2];
@@ -320,7 +325,14 @@ int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void*
         cached = it != g_plan_cache.end() && it->second == sig;
     }
     plan->gbuf.assign(static_cast<size_t>(T), nullptr);
-    for (int32_t t = 0; t < T; ++t) plan->gbuf[t] = desc[t].gbuf;
+    plan->layouts = layouts;
+    plan->fold_begin.assign(static_cast<size_t>(T), 0);
+    plan->fold_tiles.assign(static_cast<size_t>(T), 0);
+    for (int32_t t = 0; t < T; ++t) {
+        plan->gbuf[t] = desc[t].gbuf;
+        plan->fold_begin[t] = desc[t].tile_begin[0];
+        plan->fold_tiles[t] = desc[t].ntiles[0];
+    }
     plan->off = off;
     plan->geom[0] = geom[0];
     plan->geom[1] = geom[1];
@@ -782,6 +794,20 @@ namespace {
 constexpr int64_t kOffloadChunk = int64_t(1) << 22;  // elements per transfer-and-update chunk
 constexpr size_t kHostAlign = 64;
 
+// The pipelined offloaded step keeps one 32-byte partial per fold chunk after
+// the plan; a chunk holds at least one tile, so the tile bound bounds them.
+int64_t offload_chunks_bound(const std::vector<int64_t>& ns)
+{
+    int64_t b = 0;
+    for (int64_t n : ns) b += tiles_bound(n);
+    return b;
+}
+
+size_t offload_partials_offset(const std::vector<int64_t>& ns, int32_t M)
+{
+    return align_up(plan_offsets(ns, M, PlanKind::Fold).total, kAlign);
+}
+
 // Host staging of an offloaded step: the record, then every tensor's fp32
 // gradient, then every tensor's bf16 output (64-byte aligned regions).
 struct HostLayout {
@@ -839,7 +865,7 @@ size_t zero_offload_workspace_bytes(const zero_offload_tensor* tensors, int32_t 
     if (!offload_tensors_ok(tensors, T, M)) return 0;
     std::vector<int64_t> ns;
     for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
-    return plan_offsets(ns, M, PlanKind::Fold).total;
+    return offload_partials_offset(ns, M) + sizeof(zero_bucket_partial) * static_cast<size_t>(offload_chunks_bound(ns));
 }
 
 size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int32_t T)
@@ -849,6 +875,152 @@ size_t zero_offload_host_workspace_bytes(const zero_offload_tensor* tensors, int
 }
 
 }  // extern "C"
+
+// The offloaded step when the update needs nothing global (no clipping, no
+// skip, a fixed scale): the fold runs group by group (tile ranges of the fold
+// plan of one tile per CU, launched in the accumulate mode so that
+// each group leaves a stamped partial of its sum of squares), each group's
+// gradient goes down behind its fold in pieces of kOffloadChunk elements, and
+// the host updates piece k while the GPU folds and copies the next ones. The
+// record is combined from the group partials at the end. The host applies
+// grad_scale in binary32 to the staged (unscaled) fold, the product the fold
+// pass stores, so the state is the one zero_step gives; the reported sum of
+// squares combines the partials in group order instead of tile order.
+static int offload_pipelined(const zero_offload_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                             double external_sumsq, uint8_t* wsb, size_t ws_bytes, const Plan& plan, uint8_t* hb,
+                             const HostLayout& hl, zero_result* rec_d, zero_result* res_host, int32_t threads,
+                             hipStream_t stream)
+{
+    const int64_t tile_vecs = static_cast<int64_t>(kGeoms[plan.geom[0]].nt) * kGeoms[plan.geom[0]].u;
+    const int64_t tile_elems = tile_vecs * kVec;
+    const int64_t per = std::max<int64_t>(static_cast<int64_t>(compute_units()), kOffloadChunk / tile_elems);
+    struct Group {
+        int32_t t;
+        int64_t j0, j1;  // tile range within the tensor
+        int64_t b, e;    // element range its fold writes
+    };
+    struct Piece {
+        int32_t t;
+        int64_t b, e;
+        hipEvent_t ready;
+    };
+    std::vector<Group> groups;
+    for (int32_t t = 0; t < T; ++t) {
+        const Layout& L = plan.layouts[t];
+        const int64_t nt = plan.fold_tiles[t], n = tensors[t].n;
+        for (int64_t j0 = 0; j0 < nt; j0 += per) {
+            const int64_t j1 = std::min(nt, j0 + per);
+            int64_t b, e;
+            if (L.nvec >= 0) {  // tile j: vectors [j, j+1) * tile_vecs; the head with tile 0, the tail with the last
+                b = j0 == 0 ? 0 : L.head + j0 * tile_elems;
+                e = j1 == nt ? n : L.head + j1 * tile_elems;
+            } else {
+                b = j0 * tile_elems;
+                e = std::min(n, j1 * tile_elems);
+            }
+            groups.push_back(Group{t, j0, j1, b, e});
+        }
+    }
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
+    const size_t poff = offload_partials_offset(ns, M);
+    if (ws_bytes < poff + sizeof(zero_bucket_partial) * groups.size()) return ZERO_ERR_WORKSPACE_TOO_SMALL;
+    zero_bucket_partial* parts_d = reinterpret_cast<zero_bucket_partial*>(wsb + poff);
+    zero_result* rec_h = reinterpret_cast<zero_result*>(hb);
+    zero_bucket_partial* first_h = reinterpret_cast<zero_bucket_partial*>(hb + sizeof(zero_result));
+    static std::atomic<uint64_t> g_stamps{1};
+    const uint64_t stamp = g_stamps.fetch_add(1);
+    const float gscale = static_cast<float>(hp->grad_scale);
+    hipStream_t up = copy_stream();
+    if (up == nullptr) return ZERO_ERR_HIP;
+
+    // ---- every group's fold and its pieces down, then the record, all on `stream`
+    int status = ZERO_OK;
+    std::vector<Piece> pieces;
+    for (size_t c = 0; c < groups.size() && status == ZERO_OK; ++c) {
+        const Group& k = groups[c];
+        const int64_t tb = plan.fold_begin[k.t] + k.j0;
+        FinalizeArgs fin{};
+        fin.counter = plan.counter;
+        fin.slot = parts_d + c;
+        fin.stamp = stamp;
+        fin.accumulate = 0;
+        fin.final = 1;
+        if (launch_fused(Mode::Acc, plan.geom[0], plan.hdr, plan.desc, plan.map0 + tb, k.j1 - k.j0, plan.sig, M,
+                         gscale, AdamScalars{}, plan.parts + tb, fin, nullptr, stream) != hipSuccess ||
+            (c == 0 && hipMemcpyAsync(first_h, parts_d, sizeof(zero_bucket_partial), hipMemcpyDeviceToHost,
+                                      stream) != hipSuccess)) {
+            status = ZERO_ERR_HIP;
+            break;
+        }
+        for (int64_t b = k.b; b < k.e && status == ZERO_OK; b += kOffloadChunk) {
+            Piece q{k.t, b, std::min(k.e, b + kOffloadChunk), nullptr};
+            if (hipEventCreateWithFlags(&q.ready, hipEventDisableTiming) != hipSuccess) {
+                status = ZERO_ERR_HIP;
+                break;
+            }
+            pieces.push_back(q);
+            float* g_h = reinterpret_cast<float*>(hb + hl.g[q.t]) + q.b;
+            if (hipMemcpyAsync(g_h, plan.gbuf[q.t] + q.b, 4 * static_cast<size_t>(q.e - q.b), hipMemcpyDeviceToHost,
+                               stream) != hipSuccess ||
+                hipEventRecord(q.ready, stream) != hipSuccess)
+                status = ZERO_ERR_HIP;
+        }
+    }
+    if (status == ZERO_OK &&
+        (launch_bucket_finalize(plan.hdr, plan.sig, parts_d, static_cast<int32_t>(groups.size()), stamp, gscale,
+                                nullptr, external_sumsq, hp->max_grad_norm, 0, rec_d, stream) != hipSuccess ||
+         hipMemcpyAsync(rec_h, rec_d, sizeof(zero_result), hipMemcpyDeviceToHost, stream) != hipSuccess))
+        status = ZERO_ERR_HIP;
+
+    // ---- the host update piece by piece, each bf16 piece up on the copy stream
+    bool stale = false;
+    if (status == ZERO_OK) {
+        TeamSlot& slot = team_slot(team_size(threads));
+        std::lock_guard<std::mutex> lk(slot.use);
+        ThreadTeam& team = *slot.team;
+        HostAdamScalars sc = host_scalars(hp, 1.0);
+        sc.gscale = gscale;
+        for (size_t c = 0; c < pieces.size(); ++c) {
+            const Piece& q = pieces[c];
+            if (hipEventSynchronize(q.ready) != hipSuccess) {
+                status = ZERO_ERR_HIP;
+                break;
+            }
+            // a workspace that no longer holds the plan poisons every stamp:
+            // then nothing is updated and the record says so
+            if (c == 0 && first_h->stamp != stamp) {
+                stale = true;
+                break;
+            }
+            const zero_offload_tensor& x = tensors[q.t];
+            const float* g_h = reinterpret_cast<const float*>(hb + hl.g[q.t]) + q.b;
+            uint16_t* o_h = reinterpret_cast<uint16_t*>(hb + hl.out[q.t]) + q.b;
+            host_adamw_parallel(team, x.master + q.b, x.exp_avg + q.b, x.exp_avg_sq + q.b, g_h, o_h, q.e - q.b, sc);
+            if (hipMemcpyAsync(static_cast<uint16_t*>(x.param_out) + q.b, o_h, 2 * static_cast<size_t>(q.e - q.b),
+                               hipMemcpyHostToDevice, up) != hipSuccess) {
+                status = ZERO_ERR_HIP;
+                break;
+            }
+        }
+    }
+    hipEvent_t done = nullptr;
+    if (status == ZERO_OK) {
+        if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess ||
+            hipEventRecord(done, up) != hipSuccess || hipStreamWaitEvent(stream, done, 0) != hipSuccess)
+            status = ZERO_ERR_HIP;
+    }
+    // the record (and, on any early exit, every copy still in flight)
+    const hipError_t sync = hipStreamSynchronize(stream);
+    if (status != ZERO_OK) (void)hipStreamSynchronize(up);
+    if (done != nullptr) (void)hipEventDestroy(done);
+    for (const Piece& q : pieces) (void)hipEventDestroy(q.ready);
+    if (status != ZERO_OK) return status;
+    if (sync != hipSuccess) return ZERO_ERR_HIP;
+    *res_host = *rec_h;
+    if (stale && res_host->status == ZERO_OK) res_host->status = ZERO_ERR_STALE_WORKSPACE;
+    return ZERO_OK;
+}
 
 // The offloaded step; lscfg/ls non-null for the AMP form: the fold reads
 // ls->inv_scale, always skips on a non-finite gradient, and its last
@@ -877,6 +1049,13 @@ static int offload_impl(const zero_offload_tensor* tensors, int32_t T, int32_t M
     if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ZERO_ERR_INVALID_ARGUMENT;
     if (host_ws == nullptr || reinterpret_cast<uintptr_t>(host_ws) % kHostAlign != 0)
         return ZERO_ERR_INVALID_ARGUMENT;
+    if (total_n > 0) {  // the whole size query's answer, whichever form of the step runs
+        std::vector<int64_t> ns;
+        for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
+        if (ws_bytes < offload_partials_offset(ns, M) + sizeof(zero_bucket_partial) *
+                                                             static_cast<size_t>(offload_chunks_bound(ns)))
+            return ZERO_ERR_WORKSPACE_TOO_SMALL;
+    }
     const HostLayout hl = host_layout(tensors, T);
     if (host_ws_bytes < hl.total) return ZERO_ERR_WORKSPACE_TOO_SMALL;
     uint8_t* hb = static_cast<uint8_t*>(host_ws);
@@ -895,6 +1074,9 @@ static int offload_impl(const zero_offload_tensor* tensors, int32_t T, int32_t M
         Plan plan;
         const int st = make_plan(pts, M, PlanKind::Fold, ws, ws_bytes, stream, &plan);
         if (st != ZERO_OK) return st;
+        if (!amp && !(hp->max_grad_norm > 0.0) && hp->skip_on_nonfinite == 0)
+            return offload_pipelined(tensors, T, M, hp, external_sumsq, static_cast<uint8_t*>(ws), ws_bytes, plan,
+                                     hb, hl, rec_d, res_host, threads, stream);
         FinalizeArgs fin{};
         fin.res = rec_d;
         fin.counter = plan.counter;

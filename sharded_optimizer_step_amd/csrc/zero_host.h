@@ -17,6 +17,8 @@ struct HostAdamScalars {
     double bc1, bc2;            // 1 - beta1^t, 1 - beta2^t
     double eps;
     double coef;                // clip coefficient applied to g
+    float gscale = 1.0f;        // binary32 multiplier of the staged g, applied
+                                // first (g = fl32(g * gscale)), as the GPU fold does
 };
 
 // Elements [0, n): AdamW on w, m, v (fp32, in place) from the fp32 gradient

@@ -42,14 +42,18 @@ namespace {
 // UNIT_BC: both bias corrections are exactly 1.0 (late steps: beta^t below
 // half an ulp of 1), where x / 1.0 == x for every x, so skipping the two
 // divisions changes no bit of the result.
-template <bool UNIT_BC>
+// SCALED: the staged g is the unscaled fold, multiplied here in binary32 by
+// gscale (the product the GPU's fold pass stores), before anything else.
+template <bool UNIT_BC, bool SCALED>
 void adamw_loop(float* __restrict__ w, float* __restrict__ m, float* __restrict__ v, const float* __restrict__ g,
                 uint16_t* __restrict__ out, int64_t n, const HostAdamScalars& c)
 {
     const double b1 = c.b1, omb1 = c.omb1, b2 = c.b2, omb2 = c.omb2, decay = c.decay, lr = c.lr, bc1 = c.bc1,
                  bc2 = c.bc2, eps = c.eps, coef = c.coef;
+    const float gscale = c.gscale;
     for (int64_t i = 0; i < n; ++i) {
-        const double gi = static_cast<double>(g[i]) * coef;
+        const float g32 = SCALED ? g[i] * gscale : g[i];
+        const double gi = static_cast<double>(g32) * coef;
         const double mn = b1 * static_cast<double>(m[i]) + omb1 * gi;
         const double vn = b2 * static_cast<double>(v[i]) + omb2 * gi * gi;
         const double m_hat = UNIT_BC ? mn : mn / bc1;
@@ -68,10 +72,11 @@ void adamw_loop(float* __restrict__ w, float* __restrict__ m, float* __restrict_
 void host_adamw_range(float* w, float* m, float* v, const float* g, uint16_t* out, int64_t n,
                       const HostAdamScalars& c)
 {
-    if (c.bc1 == 1.0 && c.bc2 == 1.0)
-        adamw_loop<true>(w, m, v, g, out, n, c);
+    const bool unit = c.bc1 == 1.0 && c.bc2 == 1.0;
+    if (c.gscale == 1.0f)
+        unit ? adamw_loop<true, false>(w, m, v, g, out, n, c) : adamw_loop<false, false>(w, m, v, g, out, n, c);
     else
-        adamw_loop<false>(w, m, v, g, out, n, c);
+        unit ? adamw_loop<true, true>(w, m, v, g, out, n, c) : adamw_loop<false, true>(w, m, v, g, out, n, c);
 }
 
 struct ThreadTeam::Impl {

@@ -127,3 +127,50 @@ def test_empty_offload_step_reports_the_external_norm():
     hws = z.host_workspace(z.zero_offload_host_workspace_bytes([]))
     r = z.zero_offload_step([], z.HParams(max_grad_norm=1.0), 9.0, ws, hws)
     assert r["status"] == 0 and r["grad_norm"] == 3.0 and abs(r["clip_coef"] - 1.0 / (3.0 + 1e-6)) < 1e-15
+
+
+@pytest.mark.parametrize("sizes,M,scale", [([9_000_001, 70_001, 3], 8, 2.0**-10), ([2 * 4_194_304 + 5], 3, 1.0 / 3.0),
+                                           ([5000, 1], 64, 1.0)])
+def test_pipelined_offload_equals_zero_step(sizes, M, scale):
+    # no clipping, no skip, a fixed scale: the fold runs chunk by chunk beside
+    # the host update, the host applies grad_scale to the staged fold; the
+    # state must be what zero_step gives, bit for bit, and the sum of squares
+    # (combined chunk by chunk instead of tile by tile) within the rounding of
+    # a binary64 sum
+    case = Case(sizes, M, seed=540 + M, grad_std=1e-3 / scale if scale < 1 else 1e-3)
+    d1, h1 = build(case)
+    d2, h2 = build(case)
+    hp = z.HParams(step=21, grad_scale=scale)
+    res = z.new_result()
+    z.zero_step(d1, hp, 0.0, z.workspace(z.zero_step_workspace_bytes(d1, M, hp)), res)
+    r1 = z.read_result(res)
+    ots = offload_tensors(d2, h2)
+    r2, _, _ = run_offload(ots, hp, threads=4)
+    assert r1["status"] == r2["status"] == 0 and r1["found_inf"] == r2["found_inf"] == 0 and r2["skipped"] == 0
+    n = sum(sizes)
+    assert abs(r1["sumsq"] - r2["sumsq"]) <= (1e-12 + n * 2.0**-53) * r1["sumsq"]
+    for a, o in zip(d1, ots):
+        assert bits_equal(to_np_f32(a.master), o.master.numpy())
+        assert bits_equal(to_np_f32(a.exp_avg), o.exp_avg.numpy())
+        assert bits_equal(to_np_f32(a.exp_avg_sq), o.exp_avg_sq.numpy())
+        assert np.array_equal(to_np_u16(a.param_out), to_np_u16(o.param_out))
+
+
+def test_pipelined_offload_detects_a_stale_workspace():
+    sizes, M = [300_001, 4099], 4
+    case = Case(sizes, M, seed=560)
+    dts, hts = build(case)
+    ots = offload_tensors(dts, hts)
+    hp = z.HParams(step=3)
+    r, ws, hws = run_offload(ots, hp)
+    assert r["status"] == 0
+    before = [(o.master.numpy().copy(), o.exp_avg_sq.numpy().copy(), to_np_u16(o.param_out).copy()) for o in ots]
+    ws.zero_()  # the caller reuses the workspace for something else
+    r, _, _ = run_offload(ots, hp, ws=ws, hws=hws)
+    assert r["status"] == z.ZERO_ERR_STALE_WORKSPACE
+    for o, (m0, v0, out0) in zip(ots, before):
+        assert bits_equal(o.master.numpy(), m0) and bits_equal(o.exp_avg_sq.numpy(), v0)
+        assert np.array_equal(to_np_u16(o.param_out), out0)
+    z.zero_workspace_forget(ws)
+    r, _, _ = run_offload(ots, hp, ws=ws, hws=hws)
+    assert r["status"] == 0 and not bits_equal(ots[0].master.numpy(), before[0][0])
