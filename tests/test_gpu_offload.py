@@ -55,6 +55,7 @@ def check_against(ots, new, where, stats=None):
     ([9_000_001], 8, 0.5, 1.0, 0.0),          # three transfer-and-update chunks of 4Mi elements
     ([5000, 3], 64, 0.01, 1.0 / 64, 0.25),
     ([262_144], 1, 1.0, 2.0**-16, 0.0),
+    ([70_001, 3, 5_000_000], 5, 0.0, 0.5, 1.75),  # no clipping: the pipelined fold, with the other ranks' sum
 ])
 def test_offload_step_matches_the_oracle(sizes, M, max_norm, scale, ext):
     case = Case(sizes, M, seed=500 + M, grad_std=1e-3 / scale if scale < 1 else 1e-3)
