@@ -10,7 +10,9 @@
 // "ZeRO Stage 2"; Mode::Acc folds each bucket into the caller's fp32 shard
 // accumulator, its final pass emitting the bucket's norm partial, and
 // Mode::PassB then updates from the accumulator), the CPU-offloaded step
-// (Mode::PassA alone, on the GPU's side of it) and the dynamic loss scale
+// (the GPU's side of it: Mode::PassA, or, when neither clipping nor skipping
+// has to wait for the norm, Mode::Acc over groups of tiles so that each
+// group's copy to the host starts while the next folds) and the dynamic loss scale
 // (the multiplier read from device memory, the scale moved by the fold's
 // last workgroup).
 //
