@@ -23,6 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zero_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libzero_oracle.so")
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+# Path of an already built copy of the oracle to load instead of this one. The
+# mutation check of the pins sets it in a child process to a copy built from a
+# deliberately broken source; nothing else does.
+_OVERRIDE_ENV = "ZERO_ORACLE_LIB_OVERRIDE"
 
 
 def build(force: bool = False) -> str:
@@ -73,7 +77,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = build()
+        path = os.environ.get(_OVERRIDE_ENV) or build()
         L = ctypes.CDLL(path)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.oracle_bf16_to_f32.argtypes = [vp, vp, i64]

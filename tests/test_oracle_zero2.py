@@ -125,7 +125,12 @@ def test_first_micro_batch_ignores_the_accumulator_contents():
 # The step from the accumulator
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("max_norm,scale,skip", [(0.0, 1.0, 0), (1e-2, 1.0, 0), (1.0, 2.0**-16, 1), (0.0, 0.125, 0)])
+# Scales 1/3 and 0.1 (a mean over three ranks; a non-dyadic factor) are not
+# powers of two: the product with the binary32 scale rounds, so these cases
+# also pin that the accumulated step unscales exactly as the ZeRO-1 step does,
+# in binary32 with the scale rounded to binary32 once.
+@pytest.mark.parametrize("max_norm,scale,skip", [(0.0, 1.0, 0), (1e-2, 1.0, 0), (1.0, 2.0**-16, 1), (0.0, 0.125, 0),
+                                                 (0.0, 1.0 / 3.0, 0), (1e-2, 0.1, 0)])
 def test_one_micro_batch_equals_the_zero1_step(max_norm, scale, skip):
     rng = np.random.default_rng(22)
     std = 1e-3 / scale
