@@ -319,16 +319,31 @@ __device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamSc
     }
 }
 
-// AdamW + bf16 emit of elements [e0, e0+8) from their gradient g.
-__device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0,
-                                      const float (&g)[8])
+// The fp32 master, exp_avg and exp_avg_sq of elements [e0, e0+8).
+struct State8 {
+    f32x4 w0, w1, m0, m1, v0, v1;
+};
+
+__device__ __forceinline__ State8 load_state8(const Ctx& x, int64_t e0)
 {
-    const f32x4 w0 = ld4(x.master + e0), w1 = ld4(x.master + e0 + 4);
-    const f32x4 m0 = ld4(x.m + e0), m1 = ld4(x.m + e0 + 4);
-    const f32x4 v0 = ld4(x.v + e0), v1 = ld4(x.v + e0 + 4);
-    float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    State8 q;
+    q.w0 = ld4(x.master + e0);
+    q.w1 = ld4(x.master + e0 + 4);
+    q.m0 = ld4(x.m + e0);
+    q.m1 = ld4(x.m + e0 + 4);
+    q.v0 = ld4(x.v + e0);
+    q.v1 = ld4(x.v + e0 + 4);
+    return q;
+}
+
+// AdamW + bf16 emit of elements [e0, e0+8) from their gradient g and their
+// state q as loaded.
+__device__ __forceinline__ void adam8_from(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0,
+                                           const float (&g)[8], const State8& q)
+{
+    float w[8] = {q.w0.x, q.w0.y, q.w0.z, q.w0.w, q.w1.x, q.w1.y, q.w1.z, q.w1.w};
+    float m[8] = {q.m0.x, q.m0.y, q.m0.z, q.m0.w, q.m1.x, q.m1.y, q.m1.z, q.m1.w};
+    float v[8] = {q.v0.x, q.v0.y, q.v0.z, q.v0.w, q.v1.x, q.v1.y, q.v1.z, q.v1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) adam1(g[j], k.coef, c, w[j], m[j], v[j]);
     st4(x.master + e0, f32x4{w[0], w[1], w[2], w[3]});
@@ -343,6 +358,13 @@ __device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamSca
     o.z = bf16_rne(w[4]) | (bf16_rne(w[5]) << 16);
     o.w = bf16_rne(w[6]) | (bf16_rne(w[7]) << 16);
     st_nt(x.out + e0, o);
+}
+
+// AdamW + bf16 emit of elements [e0, e0+8) from their gradient g.
+__device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e0,
+                                      const float (&g)[8])
+{
+    adam8_from(x, k, c, e0, g, load_state8(x, e0));
 }
 
 // Eight elements [e0, e0+8), 16-byte vector path.
@@ -460,47 +482,81 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
             for (int u = 0; u < U; ++u) add8(s[u], w[u]);
             __syncthreads();
         }
+        if constexpr (OP == Op::Full && U == 16) {
+            // The update in pairs of vectors: both states are loaded, then
+            // both vectors are updated, which halves the dependent round
+            // trips of the update. A lane past the shard's last vector loads
+            // the shard's first vector (it exists: nvec > 0) and stores
+            // nothing, so the loads take no per-lane branch; the scheduling
+            // barriers keep each pair's loads together, ahead of its
+            // arithmetic. (The 1024-thread geometries run four waves per
+            // SIMD, within 128 registers, where a second state does not fit.)
+            if (x.nvec > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (!ok[u]) continue;
-            const int64_t e0 = x.head + (v0 + u * 64) * kVec;
-            if constexpr (OP == Op::Acc) {
-                // the running sum of the reduce-scatter results: acc + fold
-                float a[8];
-                if (k.accumulate) {
-                    const f32x4 p = ld4(x.gin + e0), q = ld4(x.gin + e0 + 4);
-                    a[0] = p.x + s[u][0]; a[1] = p.y + s[u][1]; a[2] = p.z + s[u][2]; a[3] = p.w + s[u][3];
-                    a[4] = q.x + s[u][4]; a[5] = q.y + s[u][5]; a[6] = q.z + s[u][6]; a[7] = q.w + s[u][7];
-                } else {
+                for (int u = 0; u < U; u += 2) {
+                    const State8 qa = load_state8(x, x.head + (ok[u] ? v0 + u * 64 : 0) * kVec);
+                    const State8 qb = load_state8(x, x.head + (ok[u + 1] ? v0 + (u + 1) * 64 : 0) * kVec);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) a[j] = s[u][j];
-                }
-                st4(x.gout + e0, f32x4{a[0], a[1], a[2], a[3]});
-                st4(x.gout + e0 + 4, f32x4{a[4], a[5], a[6], a[7]});
-                if (k.final) {
+                    for (int h = 0; h < 2; ++h) {
+                        if (ok[u + h]) {
+                            float g[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float g = a[j] * k.gscale;
-                        bad |= nonfinite(g);
-                        const double d = static_cast<double>(g);
-                        acc = fma(d, d, acc);
+                            for (int j = 0; j < 8; ++j) {
+                                g[j] = s[u + h][j] * k.gscale;
+                                bad |= nonfinite(g[j]);
+                                const double d = static_cast<double>(g[j]);
+                                acc = fma(d, d, acc);
+                            }
+                            adam8_from(x, k, c, x.head + (v0 + (u + h) * 64) * kVec, g, h == 0 ? qa : qb);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-                continue;
             }
-            float g[8];
+        } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                g[j] = s[u][j] * k.gscale;
-                bad |= nonfinite(g[j]);
-                const double d = static_cast<double>(g[j]);
-                acc = fma(d, d, acc);
-            }
-            if constexpr (OP == Op::PassA) {
-                st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
-                st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
-            } else {
-                adam8(x, k, c, e0, g);
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                const int64_t e0 = x.head + (v0 + u * 64) * kVec;
+                if constexpr (OP == Op::Acc) {
+                    // the running sum of the reduce-scatter results: acc + fold
+                    float a[8];
+                    if (k.accumulate) {
+                        const f32x4 p = ld4(x.gin + e0), q = ld4(x.gin + e0 + 4);
+                        a[0] = p.x + s[u][0]; a[1] = p.y + s[u][1]; a[2] = p.z + s[u][2]; a[3] = p.w + s[u][3];
+                        a[4] = q.x + s[u][4]; a[5] = q.y + s[u][5]; a[6] = q.z + s[u][6]; a[7] = q.w + s[u][7];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) a[j] = s[u][j];
+                    }
+                    st4(x.gout + e0, f32x4{a[0], a[1], a[2], a[3]});
+                    st4(x.gout + e0 + 4, f32x4{a[4], a[5], a[6], a[7]});
+                    if (k.final) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float g = a[j] * k.gscale;
+                            bad |= nonfinite(g);
+                            const double d = static_cast<double>(g);
+                            acc = fma(d, d, acc);
+                        }
+                    }
+                    continue;
+                }
+                float g[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    g[j] = s[u][j] * k.gscale;
+                    bad |= nonfinite(g[j]);
+                    const double d = static_cast<double>(g[j]);
+                    acc = fma(d, d, acc);
+                }
+                if constexpr (OP == Op::PassA) {
+                    st4(x.gout + e0, f32x4{g[0], g[1], g[2], g[3]});
+                    st4(x.gout + e0 + 4, f32x4{g[4], g[5], g[6], g[7]});
+                } else {
+                    adam8(x, k, c, e0, g);
+                }
             }
         }
     } else {
