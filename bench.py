@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--composed", action="store_true",
                    help="the same step through the three composed entry points (zero_shard_reduce, "
                         "zero_grad_check_norm, zero_adamw_step; single-tensor workloads)")
+    p.add_argument("--no-skipped-leg", action="store_true",
+                   help="leave out the skipped-steps leg of a workload with inf injection (a trace of clean steps only)")
     p.add_argument("--amp", action="store_true",
                    help="step with zero_step_amp: the loss scale held on the device, starting at the workload's "
                         "1/grad_scale (a power of two), window 1000, hysteresis 2")
@@ -475,7 +477,8 @@ def main():
             traffic = ent["bytes_per_launch"] if not w.two_pass else ent.get("bytes_per_step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-    skipped = skipped_steps(a, w, tensors, step, res, stream) if w.inject_rate > 0 and not a.composed else None
+    skipped = (skipped_steps(a, w, tensors, step, res, stream)
+               if w.inject_rate > 0 and not a.composed and not a.no_skipped_leg else None)
     cpu = None
     if a.cpu_sample > 0:
         cpu = cpu_baseline(w, a.cpu_sample)

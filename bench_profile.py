@@ -77,8 +77,10 @@ def main():
     os.chdir(ROOT)
     os.makedirs(out, exist_ok=True)
     profiles = a.profiles_dir
+    # clean steps only: a workload with inf injection also times skipped steps
+    # by default, whose update launches exit early and would mix into the trace
     bench = ["python", "-u", "bench.py", "--workload", str(a.workload), "--cpu-sample", "0", "--steps",
-             str(a.steps), "--warmup", "2"]
+             str(a.steps), "--warmup", "2", "--no-skipped-leg"]
     calib = ["python", "-u", "bench.py", "--calib-copy", "--steps", "3"]
     rp = "rocprofv3"
     cmds = {
