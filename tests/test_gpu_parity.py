@@ -207,6 +207,30 @@ def test_zero_step_single_pass(M):
     print(f"M={M} max rel {st.max_rel} max ulp {st.max_ulp}")
 
 
+@pytest.mark.parametrize("M", [4, 20])
+def test_zero_step_single_pass_long_burst_tiles(M):
+    # The single-pass geometries with 16 vectors per thread (256 x 16 up to
+    # M = 16, 512 x 16 above) update their state two vectors at a time. The
+    # large tensor gives the grid over two tiles per CU, and its last tile
+    # ends inside a pair: 1141 vectors, so lanes 53-63 of the second wave hold
+    # the pair's first vector but not its second. Beside it, a 5-element
+    # tensor with no whole vector and a 4099-element one with a head and a
+    # tail share the launch. Every element checked.
+    tile = 32768 if M <= 16 else 65536
+    sizes = [130 * tile + 1141 * 8 + 5, 5, 4099]
+    offs = [[0] * (M + 4), [0] * (M + 4), [3] * (M + 4)]
+    case = Case(sizes, M, seed=55 + M, offsets=offs)
+    dts, hts = build(case)
+    r, _ = run_step(dts, HP_SINGLE)
+    new, ro = oracle.zero_step(hts, hp_oracle(HP_SINGLE))
+    st = Stats()
+    for i, (d, h) in enumerate(zip(dts, new)):
+        assert_tensor_matches(d, h, f"M={M} tensor {i}", st)
+    assert r["found_inf"] == 0 and r["skipped"] == 0 and r["status"] == 0
+    assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
+    print(f"M={M} max rel {st.max_rel} max ulp {st.max_ulp}")
+
+
 @pytest.mark.parametrize("max_norm,skip,scale", [(1e-3, 0, 1.0), (1.0, 0, 1.0), (0.0, 1, 1.0),
                                                  (1e-3, 1, 2.0**-16)])
 def test_zero_step_two_pass(max_norm, skip, scale):
