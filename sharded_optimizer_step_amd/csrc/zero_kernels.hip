@@ -963,6 +963,16 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
 #define ZERO_FOR_EACH_GEOM(X) \
     X(0, 256, 1) X(1, 1024, 1) X(2, 1024, 2) X(3, 1024, 4) X(4, 1024, 8) X(5, 512, 16) X(6, 256, 16)
 
+// The geometries each mode is launched with, from the plan's rules: the
+// single-pass step never takes 1024 x 8, a pass that only folds never takes
+// 256 x 16, and the update pass always runs 256 x 1. Only these are built; any
+// other pair is an error at launch.
+template <Mode MODE>
+constexpr bool geom_used(int g)
+{
+    return MODE == Mode::PassB ? g == 0 : MODE == Mode::Full ? g != 4 : g != 6;
+}
+
 template <Mode MODE>
 hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* desc, const TileRef* map, int64_t tiles,
                           uint64_t sig, int M, float gscale, const AdamScalars& c, Partial* parts,
@@ -971,9 +981,12 @@ hipError_t fused_dispatch(int geom, const PlanHeader* hdr, const TensorDesc* des
     if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const unsigned grid = static_cast<unsigned>(tiles);
     switch (geom) {
-#define ZERO_CASE(I, NTV, UV)                                                                          \
-    case I:                                                                                            \
-        fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, map, sig, M, gscale, c, parts, fin, res); \
+#define ZERO_CASE(I, NTV, UV)                                                                              \
+    case I:                                                                                                \
+        if constexpr (geom_used<MODE>(I))                                                                  \
+            fused_kernel<MODE, NTV, UV><<<grid, NTV, 0, s>>>(hdr, desc, map, sig, M, gscale, c, parts, fin, res); \
+        else                                                                                               \
+            return hipErrorInvalidValue;                                                                   \
         break;
         ZERO_FOR_EACH_GEOM(ZERO_CASE)
 #undef ZERO_CASE
