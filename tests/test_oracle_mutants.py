@@ -13,7 +13,9 @@ the harness.
 
 Mutants that cannot change any result (equivalent mutants) are left out: for
 example removing the explicit overflow-to-infinity branch of the bf16 encoder,
-whose fall-through already encodes 2^128 as the infinity pattern."""
+whose fall-through already encodes 2^128 as the infinity pattern, or moving
+its normal/subnormal test up one binade, since both branches give the
+smallest normal binade the same spacing, 2^-133."""
 import concurrent.futures as cf
 import os
 import subprocess
@@ -73,6 +75,14 @@ MUTANTS = [
     ("bf16 emit keeps one fraction bit too few",
      [("const int q = (e - 1 >= -126) ? (e - 1 - 7) : (-126 - 7);",
        "const int q = (e - 1 >= -126) ? (e - 1 - 6) : (-126 - 7);")]),
+    ("bf16 NaN codes decoded as infinities", [("        if (f != 0) return sign ? -NAN : NAN;\n", "")]),
+    ("bf16 negative zero decoded as +0",
+     [("return (float)(sign ? -mag : mag);", "return (float)(sign && mag != 0.0 ? -mag : mag);")]),
+    ("bf16 emit: normal spacing used for the largest subnormals",
+     [("const int q = (e - 1 >= -126) ? (e - 1 - 7) : (-126 - 7);",
+       "const int q = (e - 1 >= -127) ? (e - 1 - 7) : (-126 - 7);")]),
+    ("bf16 emit: exponent field off by one", [("((e - 1 + 127) << 7)", "((e - 1 + 126) << 7)")]),
+    ("bf16 emit: infinity loses its sign", [("if (isinf(x)) return (uint16_t)(s | 0x7F80);", "if (isinf(x)) return 0x7F80;")]),
     # step 3: flag and sum of squares
     ("flag misses infinities", [("if (!isfinite(g[i])) bad = 1;", "if (isnan(g[i])) bad = 1;")]),
     ("flag misses NaN", [("if (!isfinite(g[i])) bad = 1;", "if (isinf(g[i])) bad = 1;")]),
@@ -91,11 +101,16 @@ MUTANTS = [
     ("skip never taken", [("res->skipped = (found_inf && skip_on_nonfinite) ? 1 : 0;", "res->skipped = 0;")]),
     ("ZeRO-1 step ignores external_sumsq",
      [(FINALIZE_CALL, FINALIZE_CALL.replace("external_sumsq", "0.0"), 0)]),
+    ("flag reported only when the step skips",
+     [("res->found_inf = found_inf ? 1 : 0;", "res->found_inf = (found_inf && skip_on_nonfinite) ? 1 : 0;")]),
+    ("NaN clip coefficient replaced by 1", [("if (coef > 1.0) coef = 1.0;", "if (!(coef <= 1.0)) coef = 1.0;")]),
     # step 5-6: AdamW and the emit
     ("clip coefficient not applied", [("const double gi = (double)g[i] * coef;", "const double gi = (double)g[i];")]),
     ("no bias correction of m", [("const double m_hat = m / bc1;", "const double m_hat = m;")]),
     ("no bias correction of v", [("const double v_hat = v / bc2;", "const double v_hat = v;")]),
     ("bias correction of m at t + 1", [("pow(hp->beta1, t)", "pow(hp->beta1, t + 1.0)")]),
+    ("bias correction of m with beta2", [("const double bc1 = 1.0 - pow(hp->beta1, t);", "const double bc1 = 1.0 - pow(hp->beta2, t);")]),
+    ("v's bias correction under the root twice", [("const double v_hat = v / bc2;", "const double v_hat = v / sqrt(bc2);")]),
     ("eps inside the square root", [("(sqrt(v_hat) + hp->eps)", "sqrt(v_hat + hp->eps)")]),
     ("weight decay not scaled by lr", [("(1.0 - hp->lr * hp->weight_decay)", "(1.0 - hp->weight_decay)")]),
     ("weight decay dropped", [("(double)master[i] * (1.0 - hp->lr * hp->weight_decay)", "(double)master[i]")]),
@@ -123,6 +138,8 @@ MUTANTS = [
      [("        master[i] = (float)theta;\n        out[i] = bf16_round_nearest_even(master[i]);\n",
        "        out[i] = bf16_round_nearest_even(master[i]);\n        master[i] = (float)theta;\n")]),
     ("skipped ZeRO-1 step still updates", [(UPDATE_CALL, "    if (1)\n        for (int32_t t = 0; t < T; ++t)\n", 0)]),
+    ("ZeRO-1 step updates only the first tensor",
+     [("        for (int32_t t = 0; t < T; ++t)\n            oracle_adamw(", "        for (int32_t t = 0; t < 1 && t < T; ++t)\n            oracle_adamw(", 0)]),
     # ZeRO-2 accumulation
     ("accumulate always adds", [("acc[i] = accumulate ? acc[i] + s : s;", "acc[i] = acc[i] + s;")]),
     ("accumulate never adds", [("acc[i] = accumulate ? acc[i] + s : s;", "acc[i] = s;")]),
@@ -140,6 +157,7 @@ MUTANTS = [
     ("initial scale a power low", [("ldexp(1.0, c->initial_scale_power)", "ldexp(1.0, c->initial_scale_power - 1)")]),
     ("hysteresis ignored", [("if (s->overflows >= c->hysteresis) {", "if (1) {")]),
     ("hysteresis off by one", [("if (s->overflows >= c->hysteresis) {", "if (s->overflows > c->hysteresis) {")]),
+    ("floor test reversed", [("s->scale = half < c->min_scale ? c->min_scale : half;", "s->scale = half > c->min_scale ? c->min_scale : half;")]),
     ("no floor at min_loss_scale", [("s->scale = half < c->min_scale ? c->min_scale : half;", "s->scale = half;")]),
     ("clean step keeps the overflow count",
      [("        s->overflows = 0;\n        s->good_steps += 1;\n", "        s->good_steps += 1;\n")]),
