@@ -23,5 +23,6 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_legs():
     r = run("--help")
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--workload", "--zero2", "--offload", "--amp", "--composed", "--cpu-sample"):
+    for flag in ("--steps", "--warmup", "--workload", "--zero2", "--offload", "--amp", "--composed", "--cpu-sample",
+                 "--no-skipped-leg"):
         assert flag in r.stdout, flag
