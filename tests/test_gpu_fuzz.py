@@ -5,7 +5,8 @@ empty tensors, one element), a replica count, per-pointer element offsets
 (one shared misalignment per tensor, or mixed offsets that force the
 element-by-element path) and hyperparameters (clip on or off, skip, a scale),
 then runs it through the fused step, the ZeRO-2 bucket reduce + accumulated
-step, and the CPU-offloaded step. Gates as in the other parity tests."""
+step, and the CPU-offloaded step. Gates as in the other parity tests. Eight
+more cases draw lists large enough for the single-pass 16-vector geometries."""
 import math
 
 import numpy as np
@@ -115,3 +116,37 @@ def test_random_layouts_through_every_form(seed):
     for i, (o, h) in enumerate(zip(ots, new)):
         assert_state_matches(o.master.numpy(), o.exp_avg.numpy(), o.exp_avg_sq.numpy(), to_np_u16(o.param_out),
                              h.master, h.exp_avg, h.exp_avg_sq, h.param_out, f"offload {where} t{i}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_ragged_lists_on_the_long_burst_geometries(seed):
+    # Single-pass steps whose lists are large enough (over two tiles per CU)
+    # for the 16-vector geometries, with the update in pairs: every tensor's
+    # last tile ends at a random vector, so pairs with one vector in the
+    # shard and one past it occur at each tensor end; tensors of 1-8 elements
+    # (no whole vector) and mixed offsets (element by element) share the
+    # launch. Every element checked against the oracle.
+    rng = np.random.default_rng(77_000 + seed)
+    M = int(rng.choice([2, 3, 8, 17, 20]))
+    tile = 32_768 if M <= 16 else 65_536
+    sizes = []
+    while sum(sizes) < 132 * tile:
+        sizes.append(int(rng.integers(1, 3 * tile)))
+    sizes += [int(rng.integers(1, 9)) for _ in range(2)]
+    offsets = []
+    for _ in sizes:
+        if rng.random() < 0.8:
+            o = int(rng.integers(0, 8))
+            a = o % 4 + 4 * int(rng.integers(0, 2))
+            offsets.append([o] * M + [a, a, a, o])
+        else:
+            offsets.append([int(rng.integers(0, 8)) for _ in range(M + 4)])
+    hp = z.HParams(step=int(rng.choice([1, 10, 1000])), grad_scale=float(rng.choice([1.0, 0.5, 1.0 / 3.0])))
+    case = Case(sizes, M, seed=950 + seed, grad_std=1e-3, offsets=offsets, zero_state=(hp.step == 1))
+    where = f"seed {seed}: {len(sizes)} tensors, {sum(sizes)} elements, M {M}, hp {hp}"
+    dts, hts = build(case)
+    res = z.new_result()
+    z.zero_step(dts, hp, 0.0, z.workspace(z.zero_step_workspace_bytes(dts, M, hp)), res)
+    new, ro = oracle.zero_step(hts, hp_oracle(hp))
+    check_record(z.read_result(res), ro, where)
+    check_all(dts, hts, new, where)
