@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -29,6 +30,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool is_fin(double x) { return std::isfinite(x); }
 
+// The kernels multiply by grad_scale rounded to binary32 once, so that
+// rounding must be a finite normal binary32 value: a scale that rounds to 0
+// would zero every gradient, one that rounds to +inf would flag every step.
+bool scale_ok(double s)
+{
+    if (!is_fin(s) || !(s > 0.0)) return false;
+    const float f = static_cast<float>(s);
+    return std::isfinite(f) && f >= std::numeric_limits<float>::min();
+}
+
 // The other ranks' sum of squares: NaN and +inf pass into the norm (a rank
 // saw a non-finite gradient); a negative value is no sum of squares.
 bool external_ok(double x) { return !(x < 0.0); }
@@ -43,7 +54,7 @@ bool hparams_ok(const zero_adamw_hparams* hp)
     if (!is_fin(hp->weight_decay)) return false;
     if (hp->step < 1) return false;
     if (std::isnan(hp->max_grad_norm)) return false;
-    if (!is_fin(hp->grad_scale) || !(hp->grad_scale > 0.0)) return false;
+    if (!scale_ok(hp->grad_scale)) return false;
     if (hp->reserved != 0) return false;
     return true;
 }
@@ -460,7 +471,7 @@ int zero_shard_reduce(const void* const* grads, int32_t M, int64_t n, double gra
                       hipStream_t stream)
 {
     if (n < 0 || M < 1 || M > ZERO_MAX_RANKS) return ZERO_ERR_INVALID_ARGUMENT;
-    if (!is_fin(grad_scale) || !(grad_scale > 0.0)) return ZERO_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(grad_scale)) return ZERO_ERR_INVALID_ARGUMENT;
     if (n == 0) return ZERO_OK;
     if (grads == nullptr || g_out == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     std::vector<uintptr_t> b16;
@@ -599,7 +610,7 @@ static int bucket_impl(const zero_grad_shard* shards, int32_t T, int32_t M, int3
     if (T < 0 || M < 1 || M > ZERO_MAX_RANKS) return ZERO_ERR_INVALID_ARGUMENT;
     if ((flags & ~(ZERO_BUCKET_ACCUMULATE | ZERO_BUCKET_FINAL)) != 0) return ZERO_ERR_INVALID_ARGUMENT;
     const bool final = (flags & ZERO_BUCKET_FINAL) != 0;
-    if (final && (partial_dev == nullptr || !is_fin(grad_scale) || !(grad_scale > 0.0)))
+    if (final && (partial_dev == nullptr || !scale_ok(grad_scale)))
         return ZERO_ERR_INVALID_ARGUMENT;
     if (T > 0 && shards == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     int64_t total_n = 0;

@@ -99,6 +99,8 @@ def _hp(**kw):
 @pytest.mark.parametrize("kw", [dict(lr=-1.0), dict(lr=float("nan")), dict(beta1=1.0), dict(beta2=-0.1),
                                 dict(eps=-1e-8), dict(step=0), dict(grad_scale=0.0),
                                 dict(grad_scale=float("inf")), dict(max_grad_norm=float("nan")),
+                                # finite as binary64, but 0, subnormal or +inf once rounded to binary32
+                                dict(grad_scale=1e-50), dict(grad_scale=1e-40), dict(grad_scale=1e300),
                                 dict(weight_decay=float("inf"))])
 def test_bad_hparams_are_rejected_without_launch(kw):
     L = z.lib()
@@ -125,6 +127,8 @@ def test_shard_reduce_argument_checks():
     assert L.zero_shard_reduce(fake, 2, -1, 1.0, 1024, None) == 1          # n < 0
     assert L.zero_shard_reduce(fake, 2, 10, 0.0, 1024, None) == 1          # scale <= 0
     assert L.zero_shard_reduce(fake, 2, 10, float("nan"), 1024, None) == 1
+    for bad in (1e-50, 1e-40, 1e300):  # binary32 rounding 0, subnormal, +inf
+        assert L.zero_shard_reduce(fake, 2, 10, bad, 1024, None) == 1
     assert L.zero_shard_reduce(None, 2, 10, 1.0, 1024, None) == 1          # no replica array
     assert L.zero_shard_reduce(fake, 2, 10, 1.0, None, None) == 1          # no output
     nul = (ctypes.c_void_p * 2)(256, None)
@@ -295,6 +299,8 @@ def test_bucket_reduce_argument_checks():
     assert L.zero_bucket_reduce(arr, 1, 2, F, 1.0, 0, None, ws, need, None) == 1           # final, no partial
     assert L.zero_bucket_reduce(arr, 1, 2, F | A, 0.0, 0, part, ws, need, None) == 1       # final, scale <= 0
     assert L.zero_bucket_reduce(arr, 1, 2, F, float("inf"), 0, part, ws, need, None) == 1
+    assert L.zero_bucket_reduce(arr, 1, 2, F, 1e-50, 0, part, ws, need, None) == 1          # binary32 rounding 0
+    assert L.zero_bucket_reduce(arr, 1, 2, F, 1e300, 0, part, ws, need, None) == 1          # binary32 rounding inf
     assert L.zero_bucket_reduce(arr, 1, 0, A, 1.0, 0, part, ws, need, None) == 1            # M < 1
     assert L.zero_bucket_reduce(arr, -1, 2, A, 1.0, 0, part, ws, need, None) == 1
     assert L.zero_bucket_reduce(None, 1, 2, A, 1.0, 0, part, ws, need, None) == 1
