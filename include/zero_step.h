@@ -38,7 +38,9 @@
  *    memory, read during the call only.
  *  - bf16 data are raw 16-bit codes (uint16). fp32 data are IEEE binary32.
  *  - The caller owns all memory. The library allocates no device memory; it
- *    keeps a small host-side cache of workspace plans.
+ *    keeps a small host-side cache of workspace plans. (The one exception is
+ *    zero_step_noalloc's static scratch, a device array that is part of the
+ *    library's code and is loaded with it.)
  *  - Every call is asynchronous on `stream` (0 = the null stream) and returns
  *    after enqueueing. Results are device-resident.
  *  - Errors: an int status (ZERO_OK or ZERO_ERR_*). On any error nothing is
@@ -77,6 +79,8 @@ extern "C" {
                                           when a bucket partial was not written by a final
                                           zero_bucket_reduce with this stamp and grad_scale;
                                           the step then wrote nothing */
+#define ZERO_ERR_SCRATCH_TOO_SMALL 6   /* zero_step_noalloc: the call's workspace would exceed
+                                          ZERO_NOALLOC_SCRATCH_BYTES; nothing was launched */
 
 /* Largest M accepted (ranks, i.e. gradient replicas per shard). */
 #define ZERO_MAX_RANKS 65536
@@ -184,6 +188,34 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
  */
 int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
               double external_sumsq, void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream);
+
+/* Bytes of the static device workspace of zero_step_noalloc (64 MiB per GPU). */
+#define ZERO_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/*
+ * zero_step_noalloc -- zero_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the workspace is a static device array inside the
+ * library, ZERO_NOALLOC_SCRATCH_BYTES bytes on each GPU, taken when the
+ * library's code is loaded on that GPU and held until the process ends. The
+ * call itself allocates nothing (no hipMalloc, no hipFree, no allocating
+ * library routine); the caller still passes the tensors and res_dev.
+ * Arguments, results and errors as for zero_step, plus
+ * ZERO_ERR_SCRATCH_TOO_SMALL, returned before anything is launched, when
+ * zero_step_workspace_bytes(tensors, T, M, hp) exceeds the scratch: the
+ * single-pass plan takes about 12 bytes per 1024 elements plus 112 + 8*M
+ * bytes per tensor (every workload up to billions of elements fits), a
+ * two-pass plan (clipping or skipping) also holds the fp32 gradient, 4 bytes
+ * per element (up to about 16 million elements).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's plan and re-arms its own counters: calls on one GPU must be ordered
+ * (one stream, or events); calls that overlap on one GPU race and corrupt
+ * each other's results. A HIP graph that captures a call holds the scratch's
+ * address, so a replay is valid only while no other call with a different
+ * tensor list has used the scratch since the capture.
+ */
+int zero_step_noalloc(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                      double external_sumsq, zero_result* res_dev, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dynamic loss scale (AMP).

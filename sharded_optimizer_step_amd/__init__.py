@@ -16,6 +16,8 @@ Functions keep the C names:
 * ``zero_adamw_step(master, exp_avg, exp_avg_sq, g, param_out, hp, res=None)``
 * ``zero_step_workspace_bytes(tensors, M, hp)``
 * ``zero_step(tensors, hp, external_sumsq, ws, res)``
+* ``zero_step_noalloc(tensors, hp, external_sumsq, res)``: the same step with the library's static device scratch
+  as its workspace, for callers that cannot allocate
 * ``zero_loss_scale_init(cfg, ls)``, ``zero_loss_scale_update(cfg, res, ls)``
 * ``zero_step_amp_workspace_bytes(tensors, M, hp)``, ``zero_step_amp(tensors, hp, cfg, ls, external_sumsq, ws, res)``
 * ``zero_bucket_reduce_workspace_bytes(shards, M)``,
@@ -50,6 +52,8 @@ ZERO_ERR_WORKSPACE_TOO_SMALL = 2
 ZERO_ERR_HIP = 3
 ZERO_ERR_STALE_WORKSPACE = 4
 ZERO_ERR_BUCKET_PARTIALS = 5
+ZERO_ERR_SCRATCH_TOO_SMALL = 6
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 RESULT_BYTES = 32
 BUCKET_ACCUMULATE = 1
 BUCKET_FINAL = 2
@@ -62,7 +66,7 @@ EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_gr
            "zero_bucket_reduce", "zero_step_accumulated_workspace_bytes", "zero_step_accumulated",
            "zero_offload_workspace_bytes", "zero_offload_host_workspace_bytes", "zero_offload_step",
            "zero_offload_adamw_host", "zero_bucket_reduce_amp", "zero_step_accumulated_amp",
-           "zero_offload_step_amp", "zero_workspace_forget", "zero_status_string")
+           "zero_offload_step_amp", "zero_workspace_forget", "zero_status_string", "zero_step_noalloc")
 LOSS_SCALE_BYTES = 16
 
 
@@ -132,6 +136,8 @@ def lib() -> ctypes.CDLL:
         L.zero_step_workspace_bytes.restype = sz
         L.zero_step.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams), dbl, vp, sz, vp, vp]
         L.zero_step.restype = ctypes.c_int
+        L.zero_step_noalloc.argtypes = [ctypes.POINTER(_CTensor), i32, i32, ctypes.POINTER(_CHparams), dbl, vp, vp]
+        L.zero_step_noalloc.restype = ctypes.c_int
         L.zero_loss_scale_init.argtypes = [ctypes.POINTER(_CLossScaleConfig), vp, vp]
         L.zero_loss_scale_init.restype = ctypes.c_int
         L.zero_loss_scale_update.argtypes = [ctypes.POINTER(_CLossScaleConfig), vp, vp, vp]
@@ -341,6 +347,18 @@ def zero_step(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float,
     wsb = _need_ws(ws)
     _check(lib().zero_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), _ptr(ws), wsb,
                            res.data_ptr(), _stream(stream)), "zero_step")
+
+
+def zero_step_noalloc(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float, res: torch.Tensor,
+                      stream=None) -> None:
+    """zero_step with the library's static device scratch as its workspace
+    (NOALLOC_SCRATCH_BYTES per GPU): the call allocates nothing. Calls on one
+    GPU share the scratch and must be ordered."""
+    _need(res, torch.uint8, "res", RESULT_BYTES)
+    arr, keep, M = _ctensors(tensors, check=True)
+    h = hp._c()
+    _check(lib().zero_step_noalloc(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), res.data_ptr(),
+                                   _stream(stream)), "zero_step_noalloc")
 
 
 @dataclasses.dataclass

@@ -390,28 +390,40 @@ std::vector<int64_t> sizes_of(const zero_tensor* ts, int32_t T)
 // The fused step; `ls` (with its config `lscfg`) non-null for the AMP form:
 // always two-pass, always skipping on a non-finite gradient, the multiplier
 // read from the device state, which the fold's last workgroup then moves.
+// The arguments of a fused step, checked on the host (nothing launched):
+// fills the plan's tensor list and the total element count.
+int step_args(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
+              const zero_result* res_dev, std::vector<PlanTensor>* pts, int64_t* total_n)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr ||
+        !external_ok(external_sumsq))
+        return ZERO_ERR_INVALID_ARGUMENT;
+    if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    *total_n = 0;
+    pts->assign(static_cast<size_t>(T), PlanTensor{});
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_tensor& x = tensors[t];
+        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
+        (*pts)[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        (*pts)[t] = PlanTensor{x.n, x.grads, x.master, x.exp_avg, x.exp_avg_sq, x.param_out, nullptr};
+        *total_n += x.n;
+    }
+    return ZERO_OK;
+}
+
 int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp, double external_sumsq,
               void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream,
               const zero_loss_scale_config* lscfg, zero_loss_scale* ls)
 {
     // ---- arguments
-    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || !hparams_ok(hp) || res_dev == nullptr ||
-        !external_ok(external_sumsq))
-        return ZERO_ERR_INVALID_ARGUMENT;
-    if (T > 0 && tensors == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     int64_t total_n = 0;
-    std::vector<PlanTensor> pts(static_cast<size_t>(T));
-    for (int32_t t = 0; t < T; ++t) {
-        const zero_tensor& x = tensors[t];
-        if (x.n < 0) return ZERO_ERR_INVALID_ARGUMENT;
-        pts[t].n = x.n;
-        if (x.n == 0) continue;
-        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
-        for (int32_t r = 0; r < M; ++r)
-            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
-        pts[t] = PlanTensor{x.n, x.grads, x.master, x.exp_avg, x.exp_avg_sq, x.param_out, nullptr};
-        total_n += x.n;
-    }
+    std::vector<PlanTensor> pts;
+    const int arg = step_args(tensors, T, M, hp, external_sumsq, res_dev, &pts, &total_n);
+    if (arg != ZERO_OK) return arg;
     const bool amp = ls != nullptr;
     const bool two_pass = amp || two_pass_of(hp);
     const int skip = amp || hp->skip_on_nonfinite != 0;
@@ -463,6 +475,8 @@ const char* zero_status_string(int status)
     case ZERO_ERR_HIP: return "HIP runtime error";
     case ZERO_ERR_STALE_WORKSPACE: return "workspace no longer holds the plan of this call";
     case ZERO_ERR_BUCKET_PARTIALS: return "a bucket partial was not written by a final bucket reduce of this step";
+    case ZERO_ERR_SCRATCH_TOO_SMALL:
+        return "the call needs more workspace than the library's static scratch holds (ZERO_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -548,6 +562,23 @@ int zero_step(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
               void* ws, size_t ws_bytes, zero_result* res_dev, hipStream_t stream)
 {
     return step_impl(tensors, T, M, hp, external_sumsq, ws, ws_bytes, res_dev, stream, nullptr, nullptr);
+}
+
+int zero_step_noalloc(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw_hparams* hp,
+                      double external_sumsq, zero_result* res_dev, hipStream_t stream)
+{
+    static_assert(kScratchBytes == ZERO_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+    // arguments and size first: nothing is resolved or launched for a call
+    // that is invalid or cannot fit
+    int64_t total_n = 0;
+    std::vector<PlanTensor> pts;
+    const int arg = step_args(tensors, T, M, hp, external_sumsq, res_dev, &pts, &total_n);
+    if (arg != ZERO_OK) return arg;
+    const size_t need = plan_offsets(sizes_of(tensors, T), M, two_pass_of(hp) ? PlanKind::StepTwoPass : PlanKind::Step).total;
+    if (need > kScratchBytes) return ZERO_ERR_SCRATCH_TOO_SMALL;
+    void* ws = nullptr;
+    if (scratch_workspace(&ws) != hipSuccess) return ZERO_ERR_HIP;
+    return step_impl(tensors, T, M, hp, external_sumsq, ws, kScratchBytes, res_dev, stream, nullptr, nullptr);
 }
 
 int zero_loss_scale_init(const zero_loss_scale_config* cfg, zero_loss_scale* ls_dev, hipStream_t stream)

@@ -17,6 +17,9 @@ constexpr int kTileElems = kThreads * kVec;  // 2048 elements per tile
 constexpr int kInlineRanks = 64;             // rank pointers passed by value per reduce pass
 constexpr int kMaxPartials = 8192;           // per-workgroup partial records of one launch
 constexpr size_t kAlign = 256;
+// Bytes of the per-device static workspace of zero_step_noalloc (64 MiB).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;  // devices whose static workspace address is kept
 
 // binary64 scalars of one AdamW step, derived on the host.
 struct AdamScalars {
@@ -201,5 +204,8 @@ int resident_grid_reduce(int Mc, bool first);
 int resident_grid_check();
 int resident_grid_adamw();
 int compute_units();  // of the current device
+// Device address of the current device's static workspace (kScratchBytes,
+// 256-byte aligned), resolved on the first call on each device.
+hipError_t scratch_workspace(void** ptr);
 
 }  // namespace zero

@@ -1106,4 +1106,37 @@ int resident_grid_adamw() { return resident(adamw_kernel); }
 
 int compute_units() { return device_cus(); }
 
+// ------------------------------------------------------------------ static scratch
+//
+// The workspace of zero_step_noalloc: one zero_step plan (header, tensor
+// table, rank pointers, tile maps, per-tile partials and, for a two-pass
+// plan, the fp32 gradient) kept in a file-scope device array instead of
+// caller memory, for callers that cannot allocate. Each device holds its own
+// copy from the moment the library's code is loaded on it until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device
+// array: its device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// handed to kernels and copies.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_workspace(void** ptr)
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % kAlign != 0) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 }  // namespace zero

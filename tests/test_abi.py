@@ -408,3 +408,31 @@ def test_amp_forms_need_their_loss_scale():
                                    ctypes.byref(r), 0, None) == 1
     assert L.zero_offload_step_amp(off, 1, 2, ctypes.byref(h), None, ls, 0.0, ws, on, 1 << 25, hn, ctypes.byref(r),
                                    0, None) == 1
+
+
+def test_noalloc_step_rejects_before_any_device_call():
+    # zero_step_noalloc checks its arguments and its plan's size against the
+    # static scratch on the host; these calls never reach the device (the
+    # pointers are fake and there may be no GPU at all)
+    L = z.lib()
+    M = 4
+    fake = (ctypes.c_void_p * M)(*[4096 * (r + 1) for r in range(M)])
+    arr = (z._CTensor * 1)()
+    clip = _hp(max_grad_norm=1.0)  # two-pass: the plan also holds the fp32 gradient, 4 B per element
+    n_big = z.NOALLOC_SCRATCH_BYTES // 4 + 1
+    arr[0] = z._CTensor(n_big, ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p)), 1 << 20, 2 << 20, 3 << 20, 4 << 20)
+    assert L.zero_step_workspace_bytes(arr, 1, M, ctypes.byref(clip)) > z.NOALLOC_SCRATCH_BYTES
+    assert L.zero_step_noalloc(arr, 1, M, ctypes.byref(clip), 0.0, ctypes.c_void_p(256), None) == \
+        z.ZERO_ERR_SCRATCH_TOO_SMALL
+    assert "scratch" in z.zero_status_string(z.ZERO_ERR_SCRATCH_TOO_SMALL)
+    # argument errors come first
+    assert L.zero_step_noalloc(arr, 1, M, ctypes.byref(clip), 0.0, None, None) == 1          # no result record
+    assert L.zero_step_noalloc(arr, 1, 0, ctypes.byref(clip), 0.0, ctypes.c_void_p(256), None) == 1   # M < 1
+    assert L.zero_step_noalloc(arr, 1, M, ctypes.byref(clip), -1.0, ctypes.c_void_p(256), None) == 1  # external < 0
+    bad = _hp(grad_scale=1e-50)
+    assert L.zero_step_noalloc(arr, 1, M, ctypes.byref(bad), 0.0, ctypes.c_void_p(256), None) == 1
+    arr[0] = z._CTensor(10, ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p)), None, 2 << 20, 3 << 20, 4 << 20)
+    assert L.zero_step_noalloc(arr, 1, M, ctypes.byref(clip), 0.0, ctypes.c_void_p(256), None) == 1  # no master
+    # the single-pass plan of the 2e9-element shard (tables only) fits
+    assert z.zero_step_workspace_bytes_for_sizes([2_000_000_000], 8, z.HParams()) <= z.NOALLOC_SCRATCH_BYTES
+    assert z.zero_step_workspace_bytes_for_sizes([n_big], M, z.HParams(max_grad_norm=1.0)) > z.NOALLOC_SCRATCH_BYTES
