@@ -83,7 +83,9 @@ def lib():
         L.oracle_bf16_to_f32.argtypes = [vp, vp, i64]
         L.oracle_f32_to_bf16.argtypes = [vp, vp, i64]
         L.oracle_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, dbl, vp]
-        L.oracle_check.argtypes = [vp, i64, ctypes.POINTER(dbl), ctypes.POINTER(i32)]
+        L.oracle_check.argtypes = [vp, i64, ctypes.POINTER(dbl), ctypes.POINTER(dbl), ctypes.POINTER(i32)]
+        L.oracle_sumsq_total.argtypes = [dbl, dbl]
+        L.oracle_sumsq_total.restype = dbl
         L.oracle_finalize.argtypes = [dbl, dbl, i32, dbl, i32, ctypes.POINTER(_Result)]
         L.oracle_adamw.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.POINTER(_Hparams), dbl]
         L.oracle_zero_step.argtypes = [ctypes.POINTER(_Tensor), i32, i32, ctypes.POINTER(_Hparams), dbl,
@@ -175,12 +177,36 @@ def reduce(grads: Sequence[np.ndarray], grad_scale: float = 1.0) -> np.ndarray:
     return out
 
 
+class SumSq:
+    """A running sum of squares and non-finite flag over slices taken in
+    index order: the compensated pair of zero_oracle.c's step 3, so that
+    chaining slices gives exactly what one call over their concatenation
+    gives."""
+
+    def __init__(self, sumsq: float = 0.0, found_inf: int = 0):
+        self._s = ctypes.c_double(sumsq)
+        self._c = ctypes.c_double(0.0)
+        self._f = ctypes.c_int32(found_inf)
+
+    def add(self, g) -> "SumSq":
+        g = _f32(g)
+        lib().oracle_check(_p(g), g.size, ctypes.byref(self._s), ctypes.byref(self._c), ctypes.byref(self._f))
+        return self
+
+    @property
+    def sumsq(self) -> float:
+        return lib().oracle_sumsq_total(self._s.value, self._c.value)
+
+    @property
+    def found_inf(self) -> int:
+        return self._f.value
+
+
 def check(g, sumsq: float = 0.0, found_inf: int = 0):
-    g = _f32(g)
-    s = ctypes.c_double(sumsq)
-    f = ctypes.c_int32(found_inf)
-    lib().oracle_check(_p(g), g.size, ctypes.byref(s), ctypes.byref(f))
-    return s.value, f.value
+    """(sum of squares, non-finite flag) of g, continuing from a plain sum
+    sumsq and a flag (use SumSq to chain slices exactly)."""
+    st = SumSq(sumsq, found_inf).add(g)
+    return st.sumsq, st.found_inf
 
 
 def finalize(sumsq: float, external_sumsq: float, found_inf: int, max_grad_norm: float,

@@ -32,8 +32,9 @@
  *   2. unscale   g[i] = s[i] * scale32, scale32 = the scale rounded once to
  *                binary32 (AMP: the gradient is multiplied by 1/S after the
  *                sum; [5D post] 3.2 trap 3).
- *   3. check     found_inf = any g[i] not finite; sumsq = sum of g[i]^2 in
- *                binary64, in index order.
+ *   3. check     found_inf = any g[i] not finite; sumsq = sum of g[i]^2:
+ *                the exact squares added in index order with a compensated
+ *                binary64 sum (within about one rounding of the exact sum).
  *   4. finalize  norm = sqrt(sumsq + external_sumsq);
  *                coef = min(1, max_norm / (norm + 1e-6)) when max_norm > 0,
  *                else 1 (NaN propagates); skip = found_inf && skip_on_nonfinite.
@@ -181,21 +182,40 @@ void oracle_reduce(const uint16_t* const* grads, int32_t M, int64_t n, double gr
 }
 
 /* ------------------------------------------------------------------------ */
-/* Step 3: non-finite flag and sum of squares. The accumulators are in/out  */
-/* so that consecutive slices chain in index order.                         */
+/* Step 3: non-finite flag and sum of squares.                              */
 /* ------------------------------------------------------------------------ */
-
-void oracle_check(const float* g, int64_t n, double* sumsq, int32_t* found_inf)
+/*
+ * The sum of squares is the exact sum of the squares, rounded to binary64.
+ * Each square is exact in binary64 (a binary32 value has 24 significant bits,
+ * its square at most 48). The terms are added in index order with Neumaier's
+ * compensated summation (A. Neumaier, "Rundungsfehleranalyse einiger
+ * Verfahren zur Summation endlicher Summen", ZAMM 54, 1974): a second binary64
+ * word carries the rounding error of every add, and s + c is then within
+ * about one rounding of the exact sum at any length. A plain left-to-right
+ * binary64 sum is not: over the 2e9 squares of the AMP workload, whose terms
+ * have few significant bits, it drifts below the exact sum by 5e-9 relative.
+ * Once the sum is not finite the correction is no longer tracked and the
+ * result is the plain sum's inf or NaN. The pair (*sumsq, *comp) is in/out,
+ * so that consecutive slices chain in index order.
+ */
+void oracle_check(const float* g, int64_t n, double* sumsq, double* comp, int32_t* found_inf)
 {
-    double acc = *sumsq;
+    double s = *sumsq, c = *comp;
     int32_t bad = *found_inf;
     for (int64_t i = 0; i < n; ++i) {
         if (!isfinite(g[i])) bad = 1;
-        acc += (double)g[i] * (double)g[i];
+        const double x = (double)g[i] * (double)g[i];
+        const double t = s + x;
+        if (isfinite(t)) c += fabs(s) >= fabs(x) ? (s - t) + x : (x - t) + s;
+        s = t;
     }
-    *sumsq = acc;
+    *sumsq = s;
+    *comp = c;
     *found_inf = bad;
 }
+
+/* The sum that a pair (sumsq, comp) of oracle_check stands for. */
+double oracle_sumsq_total(double sumsq, double comp) { return isfinite(sumsq) ? sumsq + comp : sumsq; }
 
 /* ------------------------------------------------------------------------ */
 /* Step 4: norm, clip coefficient, skip decision.                           */
@@ -278,15 +298,16 @@ int32_t oracle_zero_step(const oracle_tensor* ts, int32_t T, int32_t M, const or
 {
     float** gs = (float**)calloc((size_t)(T > 0 ? T : 1), sizeof(float*));
     if (!gs) return -1;
-    double sumsq = 0.0;
+    double sumsq = 0.0, comp = 0.0;
     int32_t found_inf = 0;
     int32_t rc = 0;
     for (int32_t t = 0; t < T; ++t) {
         gs[t] = (float*)malloc((size_t)(ts[t].n > 0 ? ts[t].n : 1) * sizeof(float));
         if (!gs[t]) { rc = -1; goto done; }
         oracle_reduce(ts[t].grads, M, ts[t].n, hp->grad_scale, gs[t]);
-        oracle_check(gs[t], ts[t].n, &sumsq, &found_inf);
+        oracle_check(gs[t], ts[t].n, &sumsq, &comp, &found_inf);
     }
+    sumsq = oracle_sumsq_total(sumsq, comp);
     oracle_finalize(sumsq, external_sumsq, found_inf, hp->max_grad_norm, hp->skip_on_nonfinite, res);
     if (!res->skipped)
         for (int32_t t = 0; t < T; ++t)
@@ -332,15 +353,16 @@ int32_t oracle_zero_step_accumulated(const oracle_acc_tensor* ts, int32_t T, con
     float** gs = (float**)calloc((size_t)(T > 0 ? T : 1), sizeof(float*));
     if (!gs) return -1;
     const float scale = (float)hp->grad_scale;
-    double sumsq = 0.0;
+    double sumsq = 0.0, comp = 0.0;
     int32_t found_inf = 0;
     int32_t rc = 0;
     for (int32_t t = 0; t < T; ++t) {
         gs[t] = (float*)malloc((size_t)(ts[t].n > 0 ? ts[t].n : 1) * sizeof(float));
         if (!gs[t]) { rc = -1; goto done; }
         for (int64_t i = 0; i < ts[t].n; ++i) gs[t][i] = ts[t].grad_acc[i] * scale;
-        oracle_check(gs[t], ts[t].n, &sumsq, &found_inf);
+        oracle_check(gs[t], ts[t].n, &sumsq, &comp, &found_inf);
     }
+    sumsq = oracle_sumsq_total(sumsq, comp);
     oracle_finalize(sumsq, external_sumsq, found_inf, hp->max_grad_norm, hp->skip_on_nonfinite, res);
     if (!res->skipped)
         for (int32_t t = 0; t < T; ++t)

@@ -86,9 +86,17 @@ MUTANTS = [
     # step 3: flag and sum of squares
     ("flag misses infinities", [("if (!isfinite(g[i])) bad = 1;", "if (isnan(g[i])) bad = 1;")]),
     ("flag misses NaN", [("if (!isfinite(g[i])) bad = 1;", "if (isinf(g[i])) bad = 1;")]),
-    ("sum of |g| instead of g^2", [("acc += (double)g[i] * (double)g[i];", "acc += fabs((double)g[i]);")]),
-    ("squares taken in binary32", [("acc += (double)g[i] * (double)g[i];", "acc += (double)(g[i] * g[i]);")]),
-    ("sum of squares not chained across tensors", [("double acc = *sumsq;", "double acc = 0.0;")]),
+    ("sum of |g| instead of g^2", [("const double x = (double)g[i] * (double)g[i];",
+                                     "const double x = fabs((double)g[i]);")]),
+    ("squares taken in binary32", [("const double x = (double)g[i] * (double)g[i];",
+                                    "const double x = (double)(g[i] * g[i]);")]),
+    ("sum of squares not chained across tensors", [("double s = *sumsq, c = *comp;", "double s = 0.0, c = *comp;")]),
+    ("plain left-to-right sum of squares (no compensation)",
+     [("if (isfinite(t)) c += fabs(s) >= fabs(x) ? (s - t) + x : (x - t) + s;", "(void)x;")]),
+    ("compensation with the operands' roles swapped",
+     [("if (isfinite(t)) c += fabs(s) >= fabs(x) ? (s - t) + x : (x - t) + s;",
+       "if (isfinite(t)) c += fabs(s) >= fabs(x) ? (x - t) + s : (s - t) + x;")]),
+    ("compensation dropped from the total", [("return isfinite(sumsq) ? sumsq + comp : sumsq;", "return sumsq;")]),
     ("flag not chained across tensors", [("int32_t bad = *found_inf;", "int32_t bad = 0;")]),
     # step 4: finalize
     ("external sum of squares dropped", [("const double total = sumsq + external_sumsq;", "const double total = sumsq;")]),

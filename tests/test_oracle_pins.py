@@ -288,10 +288,31 @@ def test_sumsq_matches_exact_rational():
 def test_sumsq_chains_across_slices_in_index_order():
     g = (RNG.standard_normal(100000) * 1e-4).astype(np.float32)
     s_all, _ = oracle.check(g)
-    s, f = 0.0, 0
+    st = oracle.SumSq()
     for k in range(0, g.size, 9973):
-        s, f = oracle.check(g[k:k + 9973], s, f)
-    assert s == s_all
+        st.add(g[k:k + 9973])
+    assert st.sumsq == s_all and st.found_inf == 0
+
+
+def test_sumsq_is_the_exact_sum_where_a_plain_sum_drops_terms():
+    # 1024^2 = 2^20 first, then 100,000 squares of 2^-17 (2^-34 each): every
+    # small square is a quarter of an ulp of 2^20, so a plain left-to-right
+    # binary64 sum never leaves 2^20; the exact sum, 2^20 + 100,000 * 2^-34,
+    # is representable, and the oracle must return it
+    g = np.concatenate([[np.float32(1024.0)], np.full(100_000, np.float32(2.0**-17))]).astype(np.float32)
+    s, f = oracle.check(g)
+    assert f == 0
+    assert s == 2.0**20 + 100_000 * 2.0**-34 != 2.0**20
+    assert s == math.fsum(float(x) * float(x) for x in g)
+
+
+def test_sumsq_of_many_terms_is_correctly_rounded():
+    # 2^20 squares of wide-range binary32 values: within one binary64 ulp of
+    # the correctly rounded exact sum (math.fsum)
+    g = (RNG.standard_normal(1 << 20) * np.exp(RNG.uniform(-8, 8, 1 << 20))).astype(np.float32)
+    s, _ = oracle.check(g)
+    exact = math.fsum((g.astype(np.float64) ** 2).tolist())
+    assert abs(s - exact) <= math.ulp(exact)
 
 
 def test_norm_of_constant_vector_closed_form():
@@ -336,10 +357,10 @@ def test_nonfinite_is_flagged(bad):
 def test_clip_matches_torch_clip_grad_norm(max_norm, std):
     sizes = [513, 4096, 37]
     gs = [(RNG.standard_normal(k) * std).astype(np.float32) for k in sizes]
-    s, f = 0.0, 0
+    st = oracle.SumSq()
     for g in gs:
-        s, f = oracle.check(g, s, f)
-    r = oracle.finalize(s, 0.0, f, max_norm, 0)
+        st.add(g)
+    r = oracle.finalize(st.sumsq, 0.0, st.found_inf, max_norm, 0)
     ps = [torch.zeros(k, dtype=torch.float64, requires_grad=True) for k in sizes]
     for p, g in zip(ps, gs):
         p.grad = torch.from_numpy(g.astype(np.float64))
