@@ -127,6 +127,22 @@ class Stats:
 ULP_GATE = 4
 
 
+def ulp_gate(*records):
+    """ULP_GATE when the device and the oracle took bit-identical clip
+    coefficients in every step given -- records are pairs (device record dict,
+    oracle Result) -- else None. The ulp gate applies where both sides evaluate
+    the same binary64 formula on the same inputs; where the coefficients
+    differ in their last bits (sums of squares in different orders) and the
+    update cancels, a stored value can move by many ulps while the absolute
+    difference stays tiny, and only the stated tolerance applies (the
+    full-size tests instead let off only the elements where the oracle itself
+    is that sensitive: coef_sensitive)."""
+    for r, ro in records:
+        if not (r["clip_coef"] == ro.clip_coef):
+            return None
+    return ULP_GATE
+
+
 def assert_state_matches(got_master, got_m, got_v, got_out, want_master, want_m, want_v, want_out, where="",
                          stats: Optional[Stats] = None, ulp_max: Optional[int] = ULP_GATE, exempt=None):
     """The parity gates of the fp32 state and the bf16 emit:
@@ -207,9 +223,10 @@ def coef_sensitive(master, m, v, g, hp: oracle.HParams, coef: float, delta: floa
     return f
 
 
-def assert_tensor_matches(dt: z.ZeroTensor, ht: oracle.TensorState, where="", stats=None):
+def assert_tensor_matches(dt: z.ZeroTensor, ht: oracle.TensorState, where="", stats=None, ulp_max=ULP_GATE):
     assert_state_matches(to_np_f32(dt.master), to_np_f32(dt.exp_avg), to_np_f32(dt.exp_avg_sq),
-                         to_np_u16(dt.param_out), ht.master, ht.exp_avg, ht.exp_avg_sq, ht.param_out, where, stats)
+                         to_np_u16(dt.param_out), ht.master, ht.exp_avg, ht.exp_avg_sq, ht.param_out, where, stats,
+                         ulp_max=ulp_max)
 
 
 def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
@@ -304,7 +321,8 @@ def oracle_sumsq_streaming(w, slice_elems: int = 1 << 22, workers: int = 16, inj
     """The oracle's sum of squares and non-finite flag over the whole
     workload, regenerating the replicas on the host slice by slice (bounded
     memory): the folds run on host threads, and the squares are chained
-    through the slices in index order, as the oracle's own step sums them.
+    through the slices in index order, as the oracle's own step sums them
+    (its compensated pair carried from slice to slice).
     `inject` lists (tensor, rank, index) elements set to +inf."""
     inj = {}
     for (t, r, i) in inject:
@@ -314,10 +332,10 @@ def oracle_sumsq_streaming(w, slice_elems: int = 1 << 22, workers: int = 16, inj
         ti, s0, s1 = job
         return oracle.reduce(host_replicas(w, w.tensors[ti], s0, s1, inj.get(ti, ())), w.grad_scale)
 
-    total, bad = 0.0, 0
+    st = oracle.SumSq()
     for g in _in_order(_slices(w, slice_elems), one, workers, f"{w.name}: oracle sum of squares"):
-        total, bad = oracle.check(g, total, bad)
-    return total, bad
+        st.add(g)
+    return st.sumsq, st.found_inf
 
 
 def _read(t: torch.Tensor, s0: int, s1: int) -> np.ndarray:

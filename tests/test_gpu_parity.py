@@ -15,7 +15,7 @@ import oracle
 import sharded_optimizer_step_amd as z
 import synth
 from cases import (Case, Stats, assert_state_matches, assert_tensor_matches, bits_equal, build, hp_oracle,
-                   ordered32, run_step, to_np_f32, to_np_u16)
+                   ordered32, run_step, to_np_f32, to_np_u16, ulp_gate, ULP_GATE)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,8 +168,9 @@ def test_adamw_step(n, t, coef):
         assert abs(z.read_result(res)["clip_coef"] - coef) <= 1e-6 * coef
     z.zero_adamw_step(D[0], D[1], D[2], D[3], out, hp, res)
     wt, wm, wv, wo = oracle.adamw(th, m, v, g, hp_oracle(hp), coef if coef is not None else 1.0)
+    same_coef = coef is None or z.read_result(res)["clip_coef"] == coef
     assert_state_matches(to_np_f32(D[0]), to_np_f32(D[1]), to_np_f32(D[2]), to_np_u16(out), wt, wm, wv, wo,
-                         f"adamw n={n} t={t}")
+                         f"adamw n={n} t={t}", ulp_max=ULP_GATE if same_coef else None)
 
 
 def test_adamw_step_respects_a_skipped_record():
@@ -241,7 +242,7 @@ def test_zero_step_two_pass(max_norm, skip, scale):
     r, _ = run_step(dts, hp)
     new, ro = oracle.zero_step(hts, hp_oracle(hp))
     for i, (d, h) in enumerate(zip(dts, new)):
-        assert_tensor_matches(d, h, f"tensor {i}")
+        assert_tensor_matches(d, h, f"tensor {i}", ulp_max=ulp_gate((r, ro)))
     assert r["found_inf"] == 0 and r["skipped"] == 0
     assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
     assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-6 * ro.clip_coef
@@ -260,7 +261,7 @@ def test_zero_step_two_pass_with_many_tiles_per_cu():
     new, ro = oracle.zero_step(hts, hp_oracle(hp))
     st = Stats()
     for i, (d, h) in enumerate(zip(dts, new)):
-        assert_tensor_matches(d, h, f"tensor {i}", st)
+        assert_tensor_matches(d, h, f"tensor {i}", st, ulp_max=ulp_gate((r, ro)))
     assert r["found_inf"] == 0 and r["skipped"] == 0 and ro.clip_coef < 1.0
     assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
     assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-6 * ro.clip_coef
@@ -288,7 +289,7 @@ def test_zero_step_ragged_unaligned_bucket():
         r, _ = run_step(dts, hp)
         new, ro = oracle.zero_step(hts, hp_oracle(hp))
         for i, (d, h) in enumerate(zip(dts, new)):
-            assert_tensor_matches(d, h, f"tensor {i} n={sizes[i]}")
+            assert_tensor_matches(d, h, f"tensor {i} n={sizes[i]}", ulp_max=ulp_gate((r, ro)))
         assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
 
 
@@ -336,7 +337,7 @@ def test_zero_step_external_sumsq():
     r, _ = run_step(dts, hp, external=0.01)
     new, ro = oracle.zero_step(hts, hp_oracle(hp), 0.01)
     assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
-    assert_tensor_matches(dts[0], new[0])
+    assert_tensor_matches(dts[0], new[0], ulp_max=ulp_gate((r, ro)))
 
 
 def test_zero_step_is_bitwise_repeatable():
@@ -471,15 +472,17 @@ def test_consecutive_steps_on_one_workspace_each_write_their_record(sizes, M, ma
     ws = z.workspace(z.zero_step_workspace_bytes(dts, M, hp))
     res = z.new_result()
     state = hts
+    records = []
     for k, ext in enumerate([0.0, 0.5, 2.0, 0.125, 7.0]):
         hp.step = 3 + k
         z.zero_step(dts, hp, ext, ws, res)
         r = z.read_result(res)
         state, ro = oracle.zero_step(state, hp_oracle(hp), ext)
+        records.append((r, ro))
         assert r["status"] == 0 and r["found_inf"] == 0
         # 1e-9: the oracle's left-to-right fp64 sum of 4M squares is itself
         # about 1e-11 from the exact sum; the steps differ by far more.
         assert math.isclose(r["sumsq"], ro.sumsq, rel_tol=1e-9), (k, r, ro)
         assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-9 * ro.clip_coef
     for d, h in zip(dts, state):
-        assert_tensor_matches(d, h, "after 5 steps")
+        assert_tensor_matches(d, h, "after 5 steps", ulp_max=ulp_gate(*records))

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import sharded_optimizer_step_amd as z
-from cases import assert_state_matches, bits_equal, hp_oracle, to_np_f32, to_np_u16
+from cases import assert_state_matches, bits_equal, hp_oracle, to_np_f32, to_np_u16, ulp_gate
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +103,7 @@ def test_tiny_adversarial_case_on_the_gpu(case):
         assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm + 1e-30, (where, r, ro)
     assert_state_matches(to_np_f32(dt.master), to_np_f32(dt.exp_avg), to_np_f32(dt.exp_avg_sq),
                          to_np_u16(dt.param_out), new[0].master, new[0].exp_avg, new[0].exp_avg_sq,
-                         new[0].param_out, where)
+                         new[0].param_out, where, ulp_max=ulp_gate((r, ro)))
 
 
 def check_record(r, ro, where):
@@ -148,9 +148,11 @@ def test_tiny_adversarial_case_through_zero2_and_offload(case):
     z.zero_step_accumulated(ats, hp, parts, 1, 77, 0.0, z.workspace(z.zero_step_accumulated_workspace_bytes(ats)), res)
     ht = oracle.TensorState([], master.copy(), m.copy(), v.copy(), np.full(n, 0x1234, np.uint16))
     new, ro = oracle.zero_step_accumulated([want_acc], [ht], hp_oracle(hp))
-    check_record(z.read_result(res), ro, "ZeRO-2 " + where)
+    r = z.read_result(res)
+    check_record(r, ro, "ZeRO-2 " + where)
     assert_state_matches(to_np_f32(st[0]), to_np_f32(st[1]), to_np_f32(st[2]), to_np_u16(out), new[0].master,
-                         new[0].exp_avg, new[0].exp_avg_sq, new[0].param_out, "ZeRO-2 " + where)
+                         new[0].exp_avg, new[0].exp_avg_sq, new[0].param_out, "ZeRO-2 " + where,
+                         ulp_max=ulp_gate((r, ro)))
 
     # the CPU-offloaded step on the first micro-batch: the ZeRO-1 step's result
     ds = [dev_at(h, o, torch.bfloat16) for h, o in zip(mb[0], offs)]
@@ -164,4 +166,5 @@ def test_tiny_adversarial_case_through_zero2_and_offload(case):
     new, ro = oracle.zero_step([ht], hp_oracle(hp))
     check_record(r, ro, "offload " + where)
     assert_state_matches(ots[0].master.numpy(), ots[0].exp_avg.numpy(), ots[0].exp_avg_sq.numpy(), to_np_u16(out),
-                         new[0].master, new[0].exp_avg, new[0].exp_avg_sq, new[0].param_out, "offload " + where)
+                         new[0].master, new[0].exp_avg, new[0].exp_avg_sq, new[0].param_out, "offload " + where,
+                         ulp_max=ulp_gate((r, ro)))
