@@ -40,20 +40,42 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
 METRIC = "params updated/s + HBM GB/s (% of peak), fused ZeRO-1 reduce+AdamW shard step"
-KERNEL_SRC = os.path.join(ROOT, "sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
+CSRC = os.path.join(ROOT, "sharded_optimizer_step_amd", "csrc")
+# Every source that decides what runs on the device: the kernels, and the host
+# planner that picks each pass's tile geometry and launches them.
+LIBRARY_SOURCES = [os.path.join(CSRC, f) for f in ("zero_kernels.hip", "zero_api.cpp", "zero_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# How the seeded inputs are drawn (synth/): "N(0, s)" is read as zero mean,
+# standard deviation s, drawn as a scaled Irwin-Hall sum of eight 16-bit
+# uniforms from Philox4x32-10 counters; bf16 replicas are the top 16 bits
+# of the fp32 draw.
+INPUTS = ("seeded synthetic: Philox4x32-10 counters, N(0, s) read as s times an Irwin-Hall sum of 8 uniforms "
+          "(mean 0, variance 1, support +-4.9), bf16 replicas by truncation of the fp32 draw")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel source with comments and blank space removed: a
-    profile stays valid across comment edits and goes stale on any change of
-    the code itself."""
+    """Hash of the library's device kernels and host planner, comments and
+    blank space removed: a profile stays valid across comment edits and goes
+    stale on any change of the code that decides which kernels run and how."""
     import re
-    src = open(KERNEL_SRC, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
-    src = re.sub(r"//[^\n]*", " ", src)                  # line comments (the source has no '//' in strings)
-    src = " ".join(src.split())
-    return hashlib.sha256(src.encode()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in LIBRARY_SOURCES:
+        src = open(path, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                  # line comments (no '//' in these sources' strings)
+        h.update(os.path.basename(path).encode() + b"\0" + " ".join(src.split()).encode() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def parse():
@@ -137,9 +159,66 @@ def build_workload(w, stagger: int):
     return tensors
 
 
-def cpu_baseline(w, sample: int) -> dict:
+def snapshot_first_step(tensors, sample: int) -> dict:
+    """The first `sample` elements of the first tensor's state and bf16
+    output, copied to the host (after the first step from the seeded state)."""
+    import numpy as np
+    import torch
+    t = tensors[0]
+    k = min(sample, t.master.numel())
+    torch.cuda.synchronize()
+    return {"master": t.master[:k].cpu().numpy(), "exp_avg": t.exp_avg[:k].cpu().numpy(),
+            "exp_avg_sq": t.exp_avg_sq[:k].cpu().numpy(),
+            "param_out": t.param_out[:k].view(torch.int16).cpu().numpy().view(np.uint16)}
+
+
+def _ordered(x, bits: int):
+    import numpy as np
+    if bits == 32:
+        u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.int64)
+        return np.where(u >= 2**31, 2**31 - u, u)
+    u = np.ascontiguousarray(x, np.uint16).astype(np.int64)
+    return np.where(u >= 0x8000, 0x8000 - u, u)
+
+
+def parity_stats(got: dict, want) -> dict:
+    """The device's first step against the oracle's on the same elements: per
+    field the largest relative error with no floor, the largest distance in
+    units in the last place (binary32; bf16 for the output), the share of
+    elements that are bit-identical, and the verdict of the parity gates
+    (|d| <= max(2e-6 |ref|, 1e-7) and <= 4 ulp on master, m, v; <= 1 bf16 ulp
+    on the output)."""
+    import numpy as np
+    out = {"elements": int(want.master.size), "max_rel_no_floor": {}, "max_ulp": {}, "bit_identical": {}}
+    ok = True
+    for name, w in (("master", want.master), ("exp_avg", want.exp_avg), ("exp_avg_sq", want.exp_avg_sq)):
+        g = got[name]
+        gd, wd = g.astype(np.float64), w.astype(np.float64)
+        same = (gd == wd) | (np.isnan(gd) & np.isnan(wd))
+        with np.errstate(invalid="ignore", divide="ignore"):
+            err = np.where(same, 0.0, np.abs(gd - wd))
+            nz = np.abs(wd) > 0
+            rel = float(np.max(err[nz] / np.abs(wd[nz]))) if nz.any() else 0.0
+        ulp = np.where(same, 0, np.abs(_ordered(g, 32) - _ordered(w, 32)))
+        ok &= bool(np.all(same | (err <= np.maximum(2e-6 * np.abs(wd), 1e-7)))) and int(ulp.max()) <= 4
+        out["max_rel_no_floor"][name] = float(f"{rel:.3g}")
+        out["max_ulp"][name] = int(ulp.max())
+        out["bit_identical"][name] = float(f"{np.mean(same):.6f}")
+    d = np.abs(_ordered(got["param_out"], 16) - _ordered(want.param_out, 16))
+    ok &= int(d.max()) <= 1
+    out["max_ulp"]["param_out"] = int(d.max())
+    out["bit_identical"]["param_out"] = float(f"{np.mean(d == 0):.6f}")
+    out["gates"] = "pass" if ok else "FAIL"
+    return out
+
+
+def cpu_baseline(w, sample: int, first=None):
     """The oracle, as it is, on the first `sample` elements of the workload's
-    first tensor, with all M replicas, on one host core."""
+    first tensor, with all M replicas, on one host core, then on every core.
+    `first`: the device's state after its first step on the same elements
+    (snapshot_first_step); the oracle's result is compared with it when the
+    sample's step is the whole step's on those elements (no clipping, or the
+    sample is the whole shard). Returns (cpu_baseline, parity or None)."""
     import oracle
     import synth
 
@@ -155,7 +234,7 @@ def cpu_baseline(w, sample: int) -> dict:
         else np.zeros(S, np.float32)
     hp = oracle.HParams(**{k: val for k, val in w.hparams().items()})
     t0 = time.perf_counter()
-    oracle.zero_step([oracle.TensorState(grads, master, m, v, None)], hp)
+    new, _ = oracle.zero_step([oracle.TensorState(grads, master, m, v, None)], hp)
     dt = time.perf_counter() - t0
     # the same oracle on every core of the process's affinity mask: one call
     # per contiguous slice of the sample, from a thread each (ctypes releases
@@ -168,10 +247,15 @@ def cpu_baseline(w, sample: int) -> dict:
     with ThreadPoolExecutor(max_workers=k) as ex:
         list(ex.map(lambda st: oracle.zero_step([st], hp), parts))
     dt_all = time.perf_counter() - t1
-    return {"value": S / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {S:,} elements of the shard with all {w.M} replicas ({dt:.1f} s, single thread)",
-            "all_cores": {"value": S / dt_all, "cores": k,
-                          "sample": f"the same sample in {k} contiguous slices, one thread each ({dt_all:.2f} s)"}}
+    cpu = {"value": S / dt, "unit": "params/s", "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"first {S:,} elements of the shard with all {w.M} replicas ({dt:.1f} s, single thread)",
+           "all_cores": {"value": S / dt_all, "cores": k,
+                         "sample": f"the same sample in {k} contiguous slices, one thread each ({dt_all:.2f} s)"}}
+    parity = None
+    if first is not None and first["master"].size == S and (not w.hparams()["max_grad_norm"] > 0 or S == w.n_total):
+        parity = {"sample": f"first {S:,} elements of {spec.name} after the first (untimed) step from the seeded "
+                            f"state, against the oracle's step on the same elements", **parity_stats(first, new[0])}
+    return cpu, parity
 
 
 def skipped_steps(a, w, tensors, step, res, stream) -> dict:
@@ -257,8 +341,12 @@ def zero2_line(a, w, tensors) -> dict:
             ev.record(stream)
         z.zero_step_accumulated(ats, hp, parts, len(buckets), stamp, 0.0, sws, res, stream)
 
+    first = None
     for i in range(a.warmup):
         step(i)
+        if i == 0 and K == 1 and a.cpu_sample > 0:
+            # one micro-batch: the first step from the seeded state is the ZeRO-1 step's
+            first = snapshot_first_step(tensors, a.cpu_sample)
     torch.cuda.synchronize()
     r = z.read_result(res)
     if r["status"] != 0:
@@ -302,7 +390,7 @@ def zero2_line(a, w, tensors) -> dict:
            "update_ms": round(update_ms, 4), "update_gbs": round(b_update * n / (update_ms * 1e-3) / 1e9, 1),
            "roofline_kernel": dom[0],
            "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[S // 2], 4)}
-    return {"value": n / (avg_ms * 1e-3), "ms_per_step": avg_ms, "config": cfg, "roofline": roofline}
+    return {"value": n / (avg_ms * 1e-3), "ms_per_step": avg_ms, "config": cfg, "roofline": roofline, "first": first}
 
 
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction: the MI355X host link (public specification)
@@ -401,11 +489,11 @@ def main():
         if a.amp:
             sys.exit("bench.py: --zero2 and --offload run with a fixed loss scale")
         out = zero2_line(a, w, tensors) if a.zero2 else offload_line(a, w, tensors)
-        cpu = cpu_baseline(w, a.cpu_sample) if a.cpu_sample > 0 else None
+        cpu, parity = cpu_baseline(w, a.cpu_sample, out.get("first")) if a.cpu_sample > 0 else (None, None)
         line = {"metric": METRIC, "value": out["value"], "unit": "params/s", "n_gpus": 1, "steps": a.steps,
                 "warmup": a.warmup, "ms_per_step": out["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-                "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": out["config"],
-                "roofline": out["roofline"], "cpu_baseline": cpu}
+                "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": {**out["config"], "inputs": INPUTS},
+                "roofline": out["roofline"], "cpu_baseline": cpu, "parity": parity}
         print(json.dumps(line), flush=True)
         return
     hp0 = w.hparams()
@@ -445,8 +533,11 @@ def main():
             hp.step = hp0["step"] + i
             z.zero_step(tensors, hp, 0.0, ws, res, stream)
 
+    first = None
     for i in range(a.warmup):
         step(i)
+        if i == 0 and a.cpu_sample > 0:  # the first step from the seeded state, for the parity sample
+            first = snapshot_first_step(tensors, a.cpu_sample)
     torch.cuda.synchronize()
     r = z.read_result(res)
     if r["status"] != 0:
@@ -472,16 +563,17 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
         ent = tf.get(str(a.workload))
-        if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp and not a.composed:
+        if (ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and not a.amp and not a.composed
+                and not a.stagger):
             # the one fused launch of a single-pass step; both launches of a two-pass step
             traffic = ent["bytes_per_launch"] if not w.two_pass else ent.get("bytes_per_step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     skipped = (skipped_steps(a, w, tensors, step, res, stream)
                if w.inject_rate > 0 and not a.composed and not a.no_skipped_leg else None)
-    cpu = None
+    cpu, parity = None, None
     if a.cpu_sample > 0:
-        cpu = cpu_baseline(w, a.cpu_sample)
+        cpu, parity = cpu_baseline(w, a.cpu_sample, first)
     line = {
         "metric": METRIC, "value": n / (total_ms * 1e-3 / K), "unit": "params/s", "n_gpus": 1, "steps": K,
         "warmup": a.warmup, "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak",
@@ -496,8 +588,9 @@ def main():
                    **({"hbm_gbs_at_2M_plus_26": round((2 * w.M + 26) * n / (total_ms * 1e-3 / K) / 1e9, 1)}
                       if bpp != 2 * w.M + 26 else {}),
                    "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[K // 2], 4),
+                   "inputs": INPUTS,
                    **({"skipped_steps": skipped} if skipped else {})},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity,
     }
     print(json.dumps(line), flush=True)
 
