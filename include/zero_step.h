@@ -142,7 +142,13 @@ size_t zero_grad_check_norm_workspace_bytes(int64_t n);
 /*
  * zero_grad_check_norm -- non-finite check, global L2 norm, clip coefficient
  * and skip decision over an fp32 gradient g (device, n elements), written to
- * the device record res_dev. hp may be NULL (no clipping, no skip); only its
+ * the device record res_dev. The check and the skip follow the loss-scaling
+ * cycle of gsyq.cn/news/457874 section 3.2 trap 3 (a step whose unscaled
+ * gradient holds inf or NaN is not applied); the norm is global because each
+ * rank holds one shard of the summed gradient ("CS336 Lecture 7", "ZeRO
+ * Stage 1" step 2), so the other ranks' share enters as external_sumsq.
+ * Clipping by that norm is not on the pages: the coefficient is the common
+ * framework rule stated at the top of this header. hp may be NULL (no clipping, no skip); only its
  * max_grad_norm and skip_on_nonfinite are read. external_sumsq is the other
  * ranks' sum of squares for a multi-GPU caller, 0 on one GPU: NaN and +inf
  * propagate into the norm, a negative value is ZERO_ERR_INVALID_ARGUMENT (as
@@ -157,7 +163,12 @@ int zero_grad_check_norm(const float* g, int64_t n, const zero_adamw_hparams* hp
 /*
  * zero_adamw_step -- AdamW on fp32 master/exp_avg/exp_avg_sq (device, n each,
  * in place) from the fp32 gradient g (device, n), plus the bf16 emit into
- * param_out (device, n bf16 codes). hp is required (max_grad_norm and
+ * param_out (device, n bf16 codes): the local update of "CS336 Lecture 7",
+ * "ZeRO Stage 1" step 3 (rank i updates shard i with the optimizer state it
+ * alone keeps: the fp32 master copy and both moments of the table in section
+ * "训练内存的详细分析") and the bf16 payload of the all-gather in step 4; the
+ * knobs are those of the AdamW optimizer block in gsyq.cn/news/457874
+ * section 4.2, and the formula is the one stated at the top of this header. hp is required (max_grad_norm and
  * skip_on_nonfinite are ignored here). res_dev (device, may be NULL) supplies
  * clip_coef and skipped from zero_grad_check_norm: when skipped is set the
  * kernel writes nothing; when res_dev is NULL the coefficient is 1.
