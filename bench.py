@@ -93,6 +93,9 @@ def parse():
     p.add_argument("--zero2", action="store_true",
                    help="the ZeRO-2 streaming step: per-bucket zero_bucket_reduce, then zero_step_accumulated")
     p.add_argument("--micro-batches", type=int, default=1, help="--zero2: micro-batches accumulated per step")
+    p.add_argument("--fused-final", action="store_true",
+                   help="--zero2: each bucket's last micro-batch folded and applied in one pass (zero_bucket_step; "
+                        "no clipping or skipping), then zero_step_accumulated with no tensors for the record")
     p.add_argument("--streams", type=int, default=2,
                    help="--zero2: side streams the bucket reduces alternate over (1: the launch stream)")
     p.add_argument("--offload", action="store_true",
@@ -316,6 +319,13 @@ def zero2_line(a, w, tensors) -> dict:
     sws = z.workspace(z.zero_step_accumulated_workspace_bytes(ats))
     hp0 = w.hparams()
     hp = z.HParams(**hp0)
+    fused = a.fused_final
+    if fused:
+        if hp.max_grad_norm > 0 or hp.skip_on_nonfinite:
+            sys.exit("bench.py --fused-final: the workload clips or skips, so its update waits for the norm")
+        steppers = [z.BucketStepper([z.BucketTensor(tensors[t].grads, accs[t] if K > 1 else None, tensors[t].master,
+                                                    tensors[t].exp_avg, tensors[t].exp_avg_sq, tensors[t].param_out)
+                                     for t in idx], parts[32 * b:32 * b + 32]) for b, idx in enumerate(buckets)]
     res = z.new_result()
     stream = torch.cuda.current_stream()
     # buckets are independent (own accumulators, workspace and partial), so a
@@ -331,6 +341,10 @@ def zero2_line(a, w, tensors) -> dict:
             for sd in side:
                 sd.wait_stream(stream)
         for k in range(K):
+            if fused and k == K - 1:
+                for b, sp in enumerate(steppers):
+                    sp.step(z.BUCKET_ACCUMULATE if k else 0, hp, stamp, side[b % NS])
+                continue
             flags = (z.BUCKET_ACCUMULATE if k else 0) | (z.BUCKET_FINAL if k == K - 1 else 0)
             for b, rd in enumerate(reducers):
                 rd.reduce(flags, hp.grad_scale, stamp, side[b % NS])
@@ -339,7 +353,10 @@ def zero2_line(a, w, tensors) -> dict:
                 stream.wait_stream(sd)
         if ev is not None:
             ev.record(stream)
-        z.zero_step_accumulated(ats, hp, parts, len(buckets), stamp, 0.0, sws, res, stream)
+        if fused:  # the record from the bucket partials alone
+            z.zero_step_accumulated([], hp, parts, len(buckets), stamp, 0.0, None, res, stream)
+        else:
+            z.zero_step_accumulated(ats, hp, parts, len(buckets), stamp, 0.0, sws, res, stream)
 
     first = None
     for i in range(a.warmup):
@@ -367,27 +384,42 @@ def zero2_line(a, w, tensors) -> dict:
     avg_ms = total_ms / S
     # algorithmic bytes per shard parameter: the first micro-batch reads M
     # replicas and writes the fp32 sum, later ones also read it back; the
-    # step reads g and the state, writes the state and the bf16 shard
-    b_reduce = 2 * w.M * K + 4 + 8 * (K - 1)
-    b_update = 30
+    # step reads g and the state, writes the state and the bf16 shard. With
+    # the fused final pass the last micro-batch reads M replicas (and the sum
+    # of the earlier ones) and the state, and writes the state and the shard.
+    if fused:
+        b_reduce = 2 * w.M * (K - 1) + 4 + 8 * (K - 2) if K > 1 else 0
+        b_update = 2 * w.M + 26 + (4 if K > 1 else 0)
+        names = ("fused final passes", "bucket reduces")
+    else:
+        b_reduce = 2 * w.M * K + 4 + 8 * (K - 1)
+        b_update = 30
+        names = ("update", "bucket reduces")
     bpp = b_reduce + b_update
-    dom = ("update", b_update, update_ms) if update_ms >= reduce_ms else ("bucket reduces", b_reduce, reduce_ms)
+    if fused:
+        # the final passes run in the first phase, the record (a few us) in the second
+        dom = (names[0], b_update, reduce_ms + update_ms) if K == 1 else (names[0] + " and reduces", bpp,
+                                                                          reduce_ms + update_ms)
+    else:
+        dom = (names[0], b_update, update_ms) if update_ms >= reduce_ms else (names[1], b_reduce, reduce_ms)
     achieved = dom[1] * n / (dom[2] * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE) and K == 1:
-        ent = json.load(open(TRAFFIC_FILE)).get(f"{w.index}_zero2_K1")
+    if os.path.exists(TRAFFIC_FILE) and K == 1 and not a.stagger:
+        ent = json.load(open(TRAFFIC_FILE)).get(f"{w.index}_zero2_K1" + ("_fused" if fused else ""))
         if ent and ent.get("kernel_source_sha256_16") == kernel_source_hash() and ent.get("kernel") == dom[0]:
             traffic = ent["bytes_per_launch"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
     cfg = {"workload": w.name + f", ZeRO-2 streaming: {len(buckets)} buckets of reduce_bucket_size 5e7 "
-                                f"in backward order, {K} micro-batch(es)",
+                                f"in backward order, {K} micro-batch(es)"
+                                + (", the last one fused with the update" if fused else ""),
            "shard_params": n, "M": w.M, "tensors": len(w.tensors), "buckets": len(buckets), "micro_batches": K,
            "reduce_streams": NS,
            "bytes_per_param": bpp, "step_t": hp0["step"],
            "hbm_gbs": round(bpp * n / (avg_ms * 1e-3) / 1e9, 1),
-           "reduce_ms": round(reduce_ms, 4), "reduce_gbs": round(b_reduce * n / (reduce_ms * 1e-3) / 1e9, 1),
-           "update_ms": round(update_ms, 4), "update_gbs": round(b_update * n / (update_ms * 1e-3) / 1e9, 1),
+           **({"bucket_phase_ms": round(reduce_ms, 4), "record_ms": round(update_ms, 4)} if fused else
+              {"reduce_ms": round(reduce_ms, 4), "reduce_gbs": round(b_reduce * n / (reduce_ms * 1e-3) / 1e9, 1),
+               "update_ms": round(update_ms, 4), "update_gbs": round(b_update * n / (update_ms * 1e-3) / 1e9, 1)}),
            "roofline_kernel": dom[0],
            "step_ms_min": round(per_ms[0], 4), "step_ms_median": round(per_ms[S // 2], 4)}
     return {"value": n / (avg_ms * 1e-3), "ms_per_step": avg_ms, "config": cfg, "roofline": roofline, "first": first}

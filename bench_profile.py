@@ -26,7 +26,6 @@ import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "sharded_optimizer_step_amd", "csrc", "zero_kernels.hip")
 TAGS = {0: "tiny_n262144_M4", 1: "gpt2_bucket_n15554976_M8", 2: "7p5B_shard_n117187500_M64",
         3: "llama7b_ragged_n809533440_M8", 4: "amp_shard_n2e9_M8"}
 
@@ -67,6 +66,8 @@ def main():
     ap.add_argument("--profiles-dir", default="profiles", help="where the summaries go (relative)")
     ap.add_argument("--summarize-only", action="store_true", help="re-read existing raw output, run nothing")
     ap.add_argument("--zero2", action="store_true", help="profile bench.py --zero2 (one micro-batch)")
+    ap.add_argument("--fused-final", action="store_true",
+                    help="with --zero2: the fused final pass (bench.py --zero2 --fused-final)")
     a = ap.parse_args()
     if a.zero2:
         return main_zero2(a)
@@ -180,12 +181,13 @@ def main_zero2(a):
     wi = 3 if a.workload == 2 else a.workload
     w = workload(wi)
     nb = len(zero2_buckets(w))
-    out = os.path.join(a.out, f"w{wi}_zero2")
+    out = os.path.join(a.out, f"w{wi}_zero2" + ("_fused" if a.fused_final else ""))
     os.chdir(ROOT)
     os.makedirs(out, exist_ok=True)
     warm = 2
+    fused = a.fused_final
     bench = ["python", "-u", "bench.py", "--zero2", "--workload", str(wi), "--cpu-sample", "0", "--steps",
-             str(a.steps), "--warmup", str(warm)]
+             str(a.steps), "--warmup", str(warm)] + (["--fused-final"] if fused else [])
     calib = ["python", "-u", "bench.py", "--calib-copy", "--steps", "3"]
     rp = "rocprofv3"
     cmds = {
@@ -201,9 +203,12 @@ def main_zero2(a):
             run(c, f"{out}/{k}.log")
     steps = a.steps + warm
     stats = list(csv.DictReader(open(one(f"{out}/trace/run_kernel_stats.csv"))))
-    groups = {"bucket reduces": "(zero::Mode)3", "update": "(zero::Mode)2"}
+    if fused:
+        groups = {"fused final passes": "(zero::Mode)4"}
+    else:
+        groups = {"bucket reduces": "(zero::Mode)3", "update": "(zero::Mode)2"}
     n = w.n_total
-    alg = {"bucket reduces": (2 * w.M + 4) * n, "update": 30 * n}
+    alg = {"bucket reduces": (2 * w.M + 4) * n, "update": 30 * n, "fused final passes": (2 * w.M + 26) * n}
     # The bucket reduces run on two streams and overlap, so a phase's time
     # per step is its wall span in the kernel trace (first start to last end
     # of its dispatches within the step), not the sum of kernel durations.
@@ -213,9 +218,18 @@ def main_zero2(a):
     cur = []
     for r in trace:
         nm = r["Kernel_Name"]
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if fused:
+            # a step: the final passes of every bucket, then the record (bucket_finalize_kernel)
+            if "bucket_finalize_kernel" in nm:
+                if cur:
+                    spans["fused final passes"].append(max(e for _, e in cur) - min(b for b, _ in cur))
+                cur = []
+            elif "fused_kernel" in nm and groups["fused final passes"] in nm:
+                cur.append((t0, t1))
+            continue
         if "fused_kernel" not in nm:
             continue
-        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
         if groups["update"] in nm:
             if cur:
                 spans["bucket reduces"].append(max(e for _, e in cur) - min(b for b, _ in cur))
@@ -248,9 +262,14 @@ def main_zero2(a):
     fetch_b = fetch_kib * 1024 / f_fetch / steps
     write_b = write_kib * 1024 / f_write / steps
     os.makedirs(a.profiles_dir, exist_ok=True)
-    md = os.path.join(a.profiles_dir, f"zero2_bucket_reduce_and_update_{TAGS[wi]}.md")
+    md = os.path.join(a.profiles_dir, (f"zero2_fused_final_pass_{TAGS[wi]}.md" if fused else
+                                       f"zero2_bucket_reduce_and_update_{TAGS[wi]}.md"))
     with open(md, "w") as f:
-        f.write(f"# ZeRO-2 streaming step on {w.name}: {nb} bucket reduces + one update per step\n\n")
+        if fused:
+            f.write(f"# ZeRO-2 streaming step on {w.name}: {nb} fused final passes (one micro-batch, folded and "
+                    f"applied in one pass) + the record per step\n\n")
+        else:
+            f.write(f"# ZeRO-2 streaming step on {w.name}: {nb} bucket reduces + one update per step\n\n")
         f.write("Commands (repository root, MI355X, ROCm 7.2):\n\n")
         for k, c in cmds.items():
             f.write(f"    {' '.join(c)}\n")
@@ -277,7 +296,7 @@ def main_zero2(a):
         f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
     tf_path = os.path.join(a.profiles_dir, "traffic.json")
     tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
-    tf[f"{wi}_zero2_K1"] = {"kernel": dom, "kernel_source_sha256_16": src_hash(),
+    tf[f"{wi}_zero2_K1" + ("_fused" if fused else "")] = {"kernel": dom, "kernel_source_sha256_16": src_hash(),
                             "bytes_per_launch": round(fetch_b + write_b), "read_bytes": round(fetch_b),
                             "write_bytes": round(write_b), "algorithmic_bytes": alg[dom],
                             "rocprof_us_per_step": round(per[dom]["ns"] / 1e3, 2), "fetch_factor": round(f_fetch, 5),

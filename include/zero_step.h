@@ -436,6 +436,68 @@ int zero_step_accumulated_amp(const zero_acc_tensor* tensors, int32_t T, const z
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * ZeRO-2, the final micro-batch fused with the update.
+ *
+ * Without clipping and without skipping, no element's update waits for the
+ * global norm, so the last micro-batch of a bucket can be folded and applied
+ * in one pass instead of being stored to the accumulator and read back by
+ * zero_step_accumulated ("CS336 Lecture 7", "ZeRO Stage 2": each bucket is
+ * reduced to its owner as soon as backward has produced it; here its owner
+ * also updates it then). Per element of the bucket:
+ *   g   = (acc + fold(replicas)) * fl32(grad_scale)   with ZERO_BUCKET_ACCUMULATE
+ *   g   = fold(replicas) * fl32(grad_scale)           without (one micro-batch)
+ *   AdamW on master, m, v and the bf16 emit, exactly as zero_step; acc is read,
+ *   never written. The bucket's sum of squares and non-finite flag of g go to
+ *   a stamped bucket partial, as a final zero_bucket_reduce writes it.
+ * The step's result record then comes from zero_step_accumulated with no
+ * tensors (T = 0, ws may be NULL): it combines the bucket partials in index
+ * order with external_sumsq. The state equals, bit for bit, what
+ * zero_bucket_reduce (FINAL) followed by zero_step_accumulated writes.
+ * Traffic per element: 2M + 26 bytes for one micro-batch (2M + 30 with the
+ * accumulator), against 2M + 4 + 30 in two passes.
+ * ------------------------------------------------------------------------ */
+
+/* One tensor shard of a fused final bucket pass. Host memory. */
+typedef struct zero_bucket_tensor {
+    int64_t n;                /* elements in this shard, >= 0 */
+    const void* const* grads; /* HOST array of M device pointers, n bf16 each (read only) */
+    const float* grad_acc;    /* device, n fp32: the earlier micro-batches' sum, read with
+                                 ZERO_BUCKET_ACCUMULATE (may be NULL otherwise); not written */
+    float* master;            /* device, n fp32, updated in place */
+    float* exp_avg;           /* device, n fp32, updated in place */
+    float* exp_avg_sq;        /* device, n fp32, updated in place */
+    void* param_out;          /* device, n bf16 codes, written */
+} zero_bucket_tensor;
+
+/*
+ * zero_bucket_step_workspace_bytes -- workspace size for zero_bucket_step over
+ * this bucket (pointers inside `tensors` are not read); 0 on invalid arguments.
+ */
+size_t zero_bucket_step_workspace_bytes(const zero_bucket_tensor* tensors, int32_t T, int32_t M);
+
+/*
+ * zero_bucket_step -- the final micro-batch of one bucket (T tensor shards,
+ * M bf16 replicas each), folded, added to the accumulator when `flags` is
+ * ZERO_BUCKET_ACCUMULATE (0: the bucket's only micro-batch; any other bit is
+ * an error), scaled and applied with AdamW and the bf16 emit in one pass;
+ * the bucket partial *partial_dev (device, 32 bytes) gets the bucket's sum of
+ * squares and flag with `stamp` and fl32(hp->grad_scale). hp must have
+ * max_grad_norm <= 0 and skip_on_nonfinite == 0 (otherwise
+ * ZERO_ERR_INVALID_ARGUMENT: the update would have to wait for the norm).
+ * A non-finite gradient is flagged in the partial and still applied, as
+ * zero_step does without skipping. ws: device workspace of
+ * zero_bucket_step_workspace_bytes(...) bytes, 256-byte aligned, one per
+ * bucket (it caches the bucket's tables; calls that share one must not run
+ * concurrently); a workspace that no longer holds the bucket's tables is
+ * detected on the device, and then nothing is written but an invalid
+ * partial. Buckets are independent: different buckets may run on different
+ * streams.
+ */
+int zero_bucket_step(const zero_bucket_tensor* tensors, int32_t T, int32_t M, int32_t flags,
+                     const zero_adamw_hparams* hp, uint64_t stamp, zero_bucket_partial* partial_dev, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * CPU-offloaded step (ZeRO-Offload).
  *
  * "第2章 软件程序与专用硬件的结合" section 2.3.4 names ZeRO-Offload, which

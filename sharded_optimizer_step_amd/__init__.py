@@ -25,6 +25,9 @@ Functions keep the C names:
 * ``zero_step_accumulated_workspace_bytes(tensors)``,
   ``zero_step_accumulated(tensors, hp, partials, nbuckets, stamp, external_sumsq, ws, res)``,
   ``BucketReducer(shards, partial, ws=None, ls=None).reduce(flags, grad_scale, stamp)``
+* ``zero_bucket_step_workspace_bytes(tensors, M)``, ``zero_bucket_step(tensors, flags, hp, stamp, partial, ws)``,
+  ``BucketStepper(tensors, partial, ws=None).step(flags, hp, stamp)``: a bucket's final micro-batch folded and
+  applied in one pass (no clipping, no skipping); then ``zero_step_accumulated([], ...)`` writes the record
 * ``zero_offload_workspace_bytes(tensors, M)``, ``zero_offload_host_workspace_bytes(tensors)``,
   ``zero_offload_step(tensors, hp, external_sumsq, ws, host_ws, threads)``,
   ``zero_offload_adamw_host(master, exp_avg, exp_avg_sq, g, param_out, hp, clip_coef, threads)``
@@ -66,7 +69,8 @@ EXPORTS = ("zero_shard_reduce", "zero_grad_check_norm_workspace_bytes", "zero_gr
            "zero_bucket_reduce", "zero_step_accumulated_workspace_bytes", "zero_step_accumulated",
            "zero_offload_workspace_bytes", "zero_offload_host_workspace_bytes", "zero_offload_step",
            "zero_offload_adamw_host", "zero_bucket_reduce_amp", "zero_step_accumulated_amp",
-           "zero_offload_step_amp", "zero_workspace_forget", "zero_status_string", "zero_step_noalloc")
+           "zero_offload_step_amp", "zero_workspace_forget", "zero_status_string", "zero_step_noalloc",
+           "zero_bucket_step_workspace_bytes", "zero_bucket_step")
 LOSS_SCALE_BYTES = 16
 
 
@@ -89,6 +93,12 @@ class _CGradShard(ctypes.Structure):
 class _CAccTensor(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("grad_acc", ctypes.c_void_p), ("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p), ("param_out", ctypes.c_void_p)]
+
+
+class _CBucketTensor(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("grads", ctypes.POINTER(ctypes.c_void_p)), ("grad_acc", ctypes.c_void_p),
+                ("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("param_out", ctypes.c_void_p)]
 
 
 class _COffloadTensor(ctypes.Structure):
@@ -157,6 +167,11 @@ def lib() -> ctypes.CDLL:
         L.zero_step_accumulated.argtypes = [ctypes.POINTER(_CAccTensor), i32, ctypes.POINTER(_CHparams), vp, i32,
                                             u64, dbl, vp, sz, vp, vp]
         L.zero_step_accumulated.restype = ctypes.c_int
+        L.zero_bucket_step_workspace_bytes.argtypes = [ctypes.POINTER(_CBucketTensor), i32, i32]
+        L.zero_bucket_step_workspace_bytes.restype = sz
+        L.zero_bucket_step.argtypes = [ctypes.POINTER(_CBucketTensor), i32, i32, i32, ctypes.POINTER(_CHparams), u64,
+                                       vp, vp, sz, vp]
+        L.zero_bucket_step.restype = ctypes.c_int
         L.zero_offload_workspace_bytes.argtypes = [ctypes.POINTER(_COffloadTensor), i32, i32]
         L.zero_offload_workspace_bytes.restype = sz
         L.zero_offload_host_workspace_bytes.argtypes = [ctypes.POINTER(_COffloadTensor), i32]
@@ -566,6 +581,88 @@ def zero_step_accumulated(tensors: Sequence[AccTensor], hp: HParams, partials: O
     _check(lib().zero_step_accumulated(arr, len(tensors), ctypes.byref(h), _ptr(partials), int(nbuckets),
                                        int(stamp) & (2**64 - 1), float(external_sumsq), _ptr(ws), wsb,
                                        res.data_ptr(), _stream(stream)), "zero_step_accumulated")
+
+
+# ---------------------------------------------------------------- ZeRO-2, fused final pass
+
+@dataclasses.dataclass
+class BucketTensor:
+    """One tensor shard of a bucket's fused final pass: this micro-batch's M
+    bf16 replicas, the fp32 accumulator of the earlier micro-batches (read
+    with BUCKET_ACCUMULATE; may be None otherwise), the fp32 state (updated in
+    place) and the bf16 output shard."""
+    grads: List[torch.Tensor]
+    grad_acc: Optional[torch.Tensor]
+    master: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    param_out: torch.Tensor
+
+
+def _cbucket(tensors: Sequence[BucketTensor], check: bool):
+    M = len(tensors[0].grads) if tensors else 1
+    keep = []
+    arr = (_CBucketTensor * max(len(tensors), 1))()
+    for i, t in enumerate(tensors):
+        n = t.master.numel()
+        if check:
+            if len(t.grads) != M:
+                raise ValueError(f"tensor {i}: {len(t.grads)} replicas, expected {M}")
+            for r, g in enumerate(t.grads):
+                _need(g, torch.bfloat16, f"tensors[{i}].grads[{r}]", n)
+            for x, nm in ((t.master, "master"), (t.exp_avg, "exp_avg"), (t.exp_avg_sq, "exp_avg_sq")):
+                _need(x, torch.float32, f"tensors[{i}].{nm}", n)
+            if t.grad_acc is not None:
+                _need(t.grad_acc, torch.float32, f"tensors[{i}].grad_acc", n)
+            _need(t.param_out, torch.bfloat16, f"tensors[{i}].param_out", n)
+        ptrs = (ctypes.c_void_p * max(M, 1))(*[g.data_ptr() for g in t.grads])
+        keep.append(ptrs)
+        arr[i] = _CBucketTensor(n, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), _ptr(t.grad_acc),
+                                t.master.data_ptr(), t.exp_avg.data_ptr(), t.exp_avg_sq.data_ptr(),
+                                t.param_out.data_ptr())
+    return arr, keep, M
+
+
+def zero_bucket_step_workspace_bytes(tensors: Sequence[BucketTensor], M: int) -> int:
+    arr, keep, _ = _cbucket(tensors, check=False)
+    return int(lib().zero_bucket_step_workspace_bytes(arr, len(tensors), int(M)))
+
+
+def zero_bucket_step(tensors: Sequence[BucketTensor], flags: int, hp: HParams, stamp: int, partial: torch.Tensor,
+                     ws: Optional[torch.Tensor], stream=None) -> None:
+    """The final micro-batch of one bucket, folded and applied in one pass
+    (no clipping, no skipping); partial: this bucket's 32-byte record."""
+    _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
+    arr, keep, M = _cbucket(tensors, check=True)
+    h = hp._c()
+    wsb = _need_ws(ws)
+    _check(lib().zero_bucket_step(arr, len(tensors), M, int(flags), ctypes.byref(h), int(stamp) & (2**64 - 1),
+                                  partial.data_ptr(), _ptr(ws), wsb, _stream(stream)), "zero_bucket_step")
+
+
+class BucketStepper:
+    """One bucket's fused final pass marshalled once (for a loop that runs it
+    every step): step() calls zero_bucket_step with the arguments prepared
+    here. The tensors, the partial and the workspace must stay alive and at
+    the same addresses."""
+
+    def __init__(self, tensors: Sequence[BucketTensor], partial: torch.Tensor, ws: Optional[torch.Tensor] = None):
+        self._arr, self._keep, self.M = _cbucket(tensors, check=True)
+        self._tensors = list(tensors)
+        self.T = len(self._tensors)
+        _need(partial, torch.uint8, "partial", BUCKET_PARTIAL_BYTES)
+        self._partial = partial
+        if ws is None:
+            ws = workspace(zero_bucket_step_workspace_bytes(self._tensors, self.M))
+        self.ws = ws
+        self._wsp, self._wsb = _ptr(ws), _need_ws(ws)
+
+    def step(self, flags: int, hp: HParams, stamp: int, stream=None) -> None:
+        h = hp._c()
+        st = lib().zero_bucket_step(self._arr, self.T, self.M, flags, ctypes.byref(h), stamp & 0xFFFFFFFFFFFFFFFF,
+                                    self._partial.data_ptr(), self._wsp, self._wsb, _stream(stream))
+        if st != ZERO_OK:
+            raise ZeroError(st, "zero_bucket_step")
 
 
 # ---------------------------------------------------------------- CPU-offloaded step

@@ -270,7 +270,10 @@ int make_plan(const std::vector<PlanTensor>& ts, int32_t M, PlanKind kind, void*
         layouts[t] = make_layout(x.n, b16, f32);
     }
     const int cus = compute_units();
-    const int geom[2] = {folds ? pick_geom_fold(layouts, M, kind != PlanKind::Step, cus) : 0,
+    // the single-pass plans (the fused step, a bucket's fused final pass) take
+    // the single-pass fold geometry; every other fold pass only folds
+    const bool fold_only = !(kind == PlanKind::Step || kind == PlanKind::BucketStep);
+    const int geom[2] = {folds ? pick_geom_fold(layouts, M, fold_only, cus) : 0,
                          updates ? pick_geom_update(layouts, cus) : 0};
     const int64_t tile_vecs[2] = {static_cast<int64_t>(kGeoms[geom[0]].nt) * kGeoms[geom[0]].u,
                                   static_cast<int64_t>(kGeoms[geom[1]].nt) * kGeoms[geom[1]].u};
@@ -775,6 +778,63 @@ int zero_step_accumulated_amp(const zero_acc_tensor* tensors, int32_t T, const z
     if (!loss_scale_config_ok(cfg) || ls_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     return acc_step_impl(tensors, T, hp, cfg, ls_dev, partials_dev, nbuckets, stamp, external_sumsq, ws, ws_bytes,
                          res_dev, stream);
+}
+
+// ------------------------------------------------------------------ ZeRO-2, fused final pass
+
+static bool bucket_tensors_ok(const zero_bucket_tensor* ts, int32_t T, int32_t M)
+{
+    if (T < 0 || M < 1 || M > ZERO_MAX_RANKS || (T > 0 && ts == nullptr)) return false;
+    for (int32_t t = 0; t < T; ++t)
+        if (ts[t].n < 0) return false;
+    return true;
+}
+
+size_t zero_bucket_step_workspace_bytes(const zero_bucket_tensor* tensors, int32_t T, int32_t M)
+{
+    if (!bucket_tensors_ok(tensors, T, M)) return 0;
+    std::vector<int64_t> ns;
+    for (int32_t t = 0; t < T; ++t) ns.push_back(tensors[t].n);
+    return plan_offsets(ns, M, PlanKind::BucketStep).total;
+}
+
+int zero_bucket_step(const zero_bucket_tensor* tensors, int32_t T, int32_t M, int32_t flags,
+                     const zero_adamw_hparams* hp, uint64_t stamp, zero_bucket_partial* partial_dev, void* ws,
+                     size_t ws_bytes, hipStream_t stream)
+{
+    // the update cannot wait for the global norm: no clipping, no skipping
+    if (!bucket_tensors_ok(tensors, T, M) || !hparams_ok(hp) || partial_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+    if (hp->max_grad_norm > 0.0 || hp->skip_on_nonfinite != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    if ((flags & ~ZERO_BUCKET_ACCUMULATE) != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    const bool accumulate = (flags & ZERO_BUCKET_ACCUMULATE) != 0;
+    int64_t total_n = 0;
+    std::vector<PlanTensor> pts(static_cast<size_t>(T));
+    for (int32_t t = 0; t < T; ++t) {
+        const zero_bucket_tensor& x = tensors[t];
+        pts[t].n = x.n;
+        if (x.n == 0) continue;
+        if (!x.grads || !x.master || !x.exp_avg || !x.exp_avg_sq || !x.param_out) return ZERO_ERR_INVALID_ARGUMENT;
+        if (accumulate && x.grad_acc == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        for (int32_t r = 0; r < M; ++r)
+            if (x.grads[r] == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
+        // the accumulator is read only, and only when accumulating
+        pts[t] = PlanTensor{x.n, x.grads, x.master, x.exp_avg, x.exp_avg_sq, x.param_out,
+                            accumulate ? const_cast<float*>(x.grad_acc) : nullptr};
+        total_n += x.n;
+    }
+    const float gscale = static_cast<float>(hp->grad_scale);
+    if (total_n == 0) return hip_status(launch_bucket_partial_empty(partial_dev, stamp, gscale, nullptr, stream));
+    Plan plan;
+    const int st = make_plan(pts, M, PlanKind::BucketStep, ws, ws_bytes, stream, &plan);
+    if (st != ZERO_OK) return st;
+    FinalizeArgs fin{};
+    fin.counter = plan.counter;
+    fin.slot = partial_dev;
+    fin.stamp = stamp;
+    fin.accumulate = accumulate ? 1 : 0;
+    fin.final = 1;
+    return hip_status(launch_fused(Mode::BucketFull, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0],
+                                   plan.sig, M, gscale, derive(hp), plan.parts, fin, nullptr, stream));
 }
 
 // ------------------------------------------------------------------ CPU-offloaded step

@@ -110,7 +110,7 @@ struct alignas(16) PlanHeader {
 
 // What a workspace plan drives: the fused step (one or two passes), the
 // accumulation of one gradient bucket, or the step from accumulated gradients.
-enum class PlanKind : int32_t { Step = 0, StepTwoPass = 1, Bucket = 2, AccStep = 3, Fold = 4 };
+enum class PlanKind : int32_t { Step = 0, StepTwoPass = 1, Bucket = 2, AccStep = 3, Fold = 4, BucketStep = 5 };
 
 // Byte offset, in the 256-byte header region of a zero_step workspace, of the
 // arrival counter of the fold pass (zero between launches).
@@ -162,6 +162,8 @@ enum class Mode : int {
     PassA = 1,  // fold + unscale + check, store fp32 g
     PassB = 2,  // read fp32 g, times gscale, AdamW + emit (coefficient/skip from the result record)
     Acc = 3,    // fold into the fp32 accumulator; on the final pass, check + norm partials
+    BucketFull = 4,  // Full for a ZeRO-2 bucket's final micro-batch: g = (acc + fold or fold) * gscale, AdamW +
+                     // emit, norm partials into the bucket partial (no clipping, no skipping)
 };
 
 // ---- launch wrappers (zero_kernels.hip); all return a hipError_t ----------

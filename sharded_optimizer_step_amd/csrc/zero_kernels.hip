@@ -276,8 +276,10 @@ struct Scal {
     bool final;       // Acc: also check and square g = acc * gscale
 };
 
-// One element, scalar path.
-template <Op OP, int MT, bool FROM0>
+// One element, scalar path. PREADD (Full only): when k.accumulate, the fold
+// is added to the caller's accumulator x.gin before the scale (the final
+// micro-batch of a ZeRO-2 bucket, updated in the same pass).
+template <Op OP, int MT, bool FROM0, bool PREADD = false>
 __device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t e, double& acc,
                                        uint32_t& bad)
 {
@@ -300,7 +302,13 @@ __device__ __forceinline__ void do_one(const Ctx& x, const Scal& k, const AdamSc
         }
         return;
     }
-    if constexpr (OP == Op::Full || OP == Op::PassA) g = fold_one<MT, true>(x.gp, x.M, e, 0.0f) * k.gscale;
+    if constexpr (OP == Op::Full && PREADD) {
+        float a = fold_one<MT, true>(x.gp, x.M, e, 0.0f);
+        if (k.accumulate) a = x.gin[e] + a;
+        g = a * k.gscale;
+    } else if constexpr (OP == Op::Full || OP == Op::PassA) {
+        g = fold_one<MT, true>(x.gp, x.M, e, 0.0f) * k.gscale;
+    }
     if constexpr (OP == Op::Check) g = x.gin[e];
     if constexpr (OP == Op::Adam) g = x.gin[e] * k.gscale;
     if constexpr (OP != Op::Adam) {
@@ -441,7 +449,7 @@ __device__ __forceinline__ void do_tile(const Ctx& x, const Scal& k, const AdamS
 // with a workgroup barrier after each replica, so the workgroup requests
 // NT*U*16 contiguous bytes of one replica together: long runs per DRAM page
 // with 64+ concurrent replica streams.
-template <Op OP, int NT, int U>
+template <Op OP, int NT, int U, bool PREADD = false>
 __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t t, double& acc,
                                          uint32_t& bad)
 {
@@ -451,7 +459,7 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
         const int64_t base = t * kTileVecs * kVec;
         for (int j = 0; j < U * kVec; ++j) {
             const int64_t e = base + static_cast<int64_t>(j) * NT + tid;
-            if (e < x.n) do_one<OP, 0, true>(x, k, c, e, acc, bad);
+            if (e < x.n) do_one<OP, 0, true, PREADD>(x, k, c, e, acc, bad);
         }
         return;
     }
@@ -481,6 +489,33 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
 #pragma unroll
             for (int u = 0; u < U; ++u) add8(s[u], w[u]);
             __syncthreads();
+        }
+        if constexpr (PREADD) {
+            // the final micro-batch of a ZeRO-2 bucket: acc + fold, one
+            // binary32 add per element, before the scale; four vectors'
+            // accumulator loads in flight at a time
+            if (k.accumulate) {
+#pragma unroll
+                for (int u0 = 0; u0 < U; u0 += 4) {
+                    f32x4 a[4][2];
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        if (u0 + h < U && ok[u0 + h]) {
+                            const int64_t e0 = x.head + (v0 + (u0 + h) * 64) * kVec;
+                            a[h][0] = ld4(x.gin + e0);
+                            a[h][1] = ld4(x.gin + e0 + 4);
+                        }
+                    }
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        if (u0 + h < U && ok[u0 + h]) {
+                            float (&q)[8] = s[u0 + h];
+                            q[0] = a[h][0].x + q[0]; q[1] = a[h][0].y + q[1]; q[2] = a[h][0].z + q[2]; q[3] = a[h][0].w + q[3];
+                            q[4] = a[h][1].x + q[4]; q[5] = a[h][1].y + q[5]; q[6] = a[h][1].z + q[6]; q[7] = a[h][1].w + q[7];
+                        }
+                    }
+                }
+            }
         }
         bool paired = false;
         if constexpr (OP == Op::Full && U == 16) {
@@ -582,9 +617,9 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
             }
         }
     }
-    if (t == 0 && tid < x.head) do_one<OP, 0, true>(x, k, c, tid, acc, bad);
+    if (t == 0 && tid < x.head) do_one<OP, 0, true, PREADD>(x, k, c, tid, acc, bad);
     const int64_t last = x.nvec > 0 ? (x.nvec - 1) / kTileVecs : 0;
-    if (t == last && tid < x.tail) do_one<OP, 0, true>(x, k, c, x.head + x.nvec * kVec + tid, acc, bad);
+    if (t == last && tid < x.tail) do_one<OP, 0, true, PREADD>(x, k, c, x.head + x.nvec * kVec + tid, acc, bad);
 }
 
 __device__ __forceinline__ Ctx ctx_of(const TensorDesc& d, int M)
@@ -776,7 +811,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
 {
     if (hdr->signature != sig) {  // the workspace no longer holds this plan: write nothing but the record
         if (blockIdx.x == 0 && threadIdx.x == 0) {
-            if constexpr (MODE == Mode::Acc) {
+            if constexpr (MODE == Mode::Acc || MODE == Mode::BucketFull) {
                 if (fin.slot != nullptr) *fin.slot = bucket_partial(0.0, 0, ~fin.stamp, gscale);
             } else if constexpr (MODE != Mode::PassB) {
                 *fin.res = stale_record();
@@ -790,16 +825,16 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
         coef = res->clip_coef;
     }
     if (fin.scale_from != nullptr) gscale = gscale * fin.scale_from->inv_scale;  // AMP: the scale of this step
-    constexpr Op OP = MODE == Mode::Full    ? Op::Full
-                      : MODE == Mode::PassA ? Op::PassA
-                      : MODE == Mode::Acc   ? Op::Acc
-                                            : Op::Adam;
+    constexpr Op OP = MODE == Mode::Full || MODE == Mode::BucketFull ? Op::Full
+                      : MODE == Mode::PassA                          ? Op::PassA
+                      : MODE == Mode::Acc                            ? Op::Acc
+                                                                     : Op::Adam;
     const Scal k{gscale, coef, false, fin.accumulate != 0, fin.final != 0};
     double acc = 0.0;
     uint32_t bad = 0;
     const TileRef tr = map[blockIdx.x];
     const Ctx x = ctx_of(desc[tr.tensor], M);
-    big_tile<OP, NT, U>(x, k, c, tr.local, acc, bad);
+    big_tile<OP, NT, U, MODE == Mode::BucketFull>(x, k, c, tr.local, acc, bad);
     if constexpr (MODE == Mode::Acc) {
         if (!k.final) return;  // uniform over the launch
     }
@@ -815,7 +850,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
             uint32_t nbad;
             combine_published<NT>(parts, gridDim.x, sumsq, nbad);
             if (threadIdx.x == 0) {
-                if constexpr (MODE == Mode::Acc) {
+                if constexpr (MODE == Mode::Acc || MODE == Mode::BucketFull) {
                     *fin.slot = bucket_partial(sumsq, nbad, fin.stamp, gscale);
                 } else {
                     *fin.res = make_record(sumsq, nbad, fin.external, fin.max_norm, fin.skip);
@@ -979,7 +1014,7 @@ hipError_t reduce_dispatch(const RankPtrs& ptrs, int Mc, int last, float scale, 
 template <Mode MODE>
 constexpr bool geom_used(int g)
 {
-    return MODE == Mode::PassB ? g == 0 : MODE == Mode::Full ? g != 4 : g != 6;
+    return MODE == Mode::PassB ? g == 0 : (MODE == Mode::Full || MODE == Mode::BucketFull) ? g != 4 : g != 6;
 }
 
 template <Mode MODE>
@@ -1090,6 +1125,8 @@ hipError_t launch_fused(Mode mode, int geom, const PlanHeader* hdr, const Tensor
         return fused_dispatch<Mode::PassB>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
     case Mode::Acc:
         return fused_dispatch<Mode::Acc>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
+    case Mode::BucketFull:
+        return fused_dispatch<Mode::BucketFull>(geom, hdr, desc, map, tiles, sig, M, gscale, c, parts, fin, res, s);
     }
     return hipErrorInvalidValue;
 }

@@ -436,3 +436,32 @@ def test_noalloc_step_rejects_before_any_device_call():
     # the single-pass plan of the 2e9-element shard (tables only) fits
     assert z.zero_step_workspace_bytes_for_sizes([2_000_000_000], 8, z.HParams()) <= z.NOALLOC_SCRATCH_BYTES
     assert z.zero_step_workspace_bytes_for_sizes([n_big], M, z.HParams(max_grad_norm=1.0)) > z.NOALLOC_SCRATCH_BYTES
+
+
+def test_bucket_step_argument_checks():
+    # zero_bucket_step refuses, before any device call, what it cannot do in
+    # one pass (clipping, skipping), unknown flags, a missing partial and an
+    # accumulating call without accumulators
+    L = z.lib()
+    M = 2
+    fake = (ctypes.c_void_p * M)(4096, 8192)
+    arr = (z._CBucketTensor * 1)()
+    arr[0] = z._CBucketTensor(100, ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p)), None, 1 << 20, 2 << 20,
+                              3 << 20, 4 << 20)
+    need = L.zero_bucket_step_workspace_bytes(arr, 1, M)
+    assert need > 0
+    ok = _hp()
+    part, ws = ctypes.c_void_p(256), ctypes.c_void_p(1 << 24)
+    assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(_hp(max_grad_norm=1.0)), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(_hp(skip_on_nonfinite=1)), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, z.BUCKET_FINAL, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, z.BUCKET_ACCUMULATE, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(ok), 1, None, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, 0, 0, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, -1, M, 0, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(_hp(grad_scale=1e-50)), 1, part, ws, need, None) == 1
+    arr[0] = z._CBucketTensor(100, ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p)), None, None, 2 << 20,
+                              3 << 20, 4 << 20)
+    assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(ok), 1, part, ws, need, None) == 1   # no master
+    arr[0] = z._CBucketTensor(-1, None, None, None, None, None, None)
+    assert L.zero_bucket_step_workspace_bytes(arr, 1, M) == 0

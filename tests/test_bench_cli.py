@@ -25,7 +25,7 @@ def test_help_lists_the_legs():
     r = run("--help")
     assert r.returncode == 0
     for flag in ("--steps", "--warmup", "--workload", "--zero2", "--offload", "--amp", "--composed", "--cpu-sample",
-                 "--no-skipped-leg"):
+                 "--no-skipped-leg", "--fused-final"):
         assert flag in r.stdout, flag
 
 

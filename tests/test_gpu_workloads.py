@@ -268,3 +268,32 @@ def test_zero2_two_micro_batches_on_the_llama_list():
     assert st.elements == w.n_total
     print("PARITY " + json.dumps(dict(workload=w.index, what="ZeRO-2, 2 micro-batches: accumulators bit-exact and "
                                       "state, every element", grad_norm=r["grad_norm"], **st.as_dict())), flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_zero2_fused_final_pass_on_the_llama_list():
+    # the 288-tensor shard through its 97 buckets in backward order, each
+    # bucket's only micro-batch folded and applied in one pass
+    # (zero_bucket_step), the record from the bucket partials: with one
+    # micro-batch this is the fused ZeRO-1 step, checked on every element
+    w = workload(3)
+    tensors = bench.build_workload(w, 0)
+    buckets = zero2_buckets(w)
+    parts = z.new_bucket_partials(len(buckets))
+    hp = _hp(w)
+    steppers = [z.BucketStepper([z.BucketTensor(tensors[t].grads, None, tensors[t].master, tensors[t].exp_avg,
+                                                tensors[t].exp_avg_sq, tensors[t].param_out) for t in idx],
+                                parts[32 * b:32 * b + 32]) for b, idx in enumerate(buckets)]
+    for sp in steppers:
+        sp.step(0, hp, 21)
+    res = z.new_result()
+    z.zero_step_accumulated([], hp, parts, len(buckets), 21, 0.0, None, res)
+    r = z.read_result(res)
+    s, f = oracle_sumsq_streaming(w)
+    ro = oracle.finalize(s, 0.0, f, hp.max_grad_norm, hp.skip_on_nonfinite)
+    assert r["status"] == 0 and r["found_inf"] == f == 0 and r["skipped"] == 0 and r["clip_coef"] == 1.0
+    assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm, (r, ro)
+    st = Stats()
+    full_step_parity(w, tensors, hp, 1.0, 1.0, st)
+    assert st.elements == w.n_total
+    _report(w, f"ZeRO-2 fused final pass, {len(buckets)} buckets: every element", r, ro, st)
