@@ -554,16 +554,18 @@ def main():
         ls = z.new_loss_scale()
         z.zero_loss_scale_init(lscfg, ls, stream)
         ws = z.workspace(z.zero_step_amp_workspace_bytes(tensors, w.M, hp))
+        runner = z.StepRunner(tensors, ws, res)  # the tensor list marshalled once, as a training loop would
 
         def step(i):
             hp.step = hp0["step"] + i
-            z.zero_step_amp(tensors, hp, lscfg, ls, 0.0, ws, res, stream)
+            runner.step_amp(hp, lscfg, ls, 0.0, stream)
     else:
         ws = z.workspace(z.zero_step_workspace_bytes(tensors, w.M, hp))
+        runner = z.StepRunner(tensors, ws, res)  # the tensor list marshalled once, as a training loop would
 
         def step(i):
             hp.step = hp0["step"] + i
-            z.zero_step(tensors, hp, 0.0, ws, res, stream)
+            runner.step(hp, 0.0, stream)
 
     first = None
     for i in range(a.warmup):

@@ -15,7 +15,8 @@ Functions keep the C names:
 * ``zero_grad_check_norm(g, hp, external_sumsq, ws, res)``
 * ``zero_adamw_step(master, exp_avg, exp_avg_sq, g, param_out, hp, res=None)``
 * ``zero_step_workspace_bytes(tensors, M, hp)``
-* ``zero_step(tensors, hp, external_sumsq, ws, res)``
+* ``zero_step(tensors, hp, external_sumsq, ws, res)``; ``StepRunner(tensors, ws, res).step(hp, external_sumsq)``
+  (and ``.step_amp``): the same calls with the tensor list marshalled once
 * ``zero_step_noalloc(tensors, hp, external_sumsq, res)``: the same step with the library's static device scratch
   as its workspace, for callers that cannot allocate
 * ``zero_loss_scale_init(cfg, ls)``, ``zero_loss_scale_update(cfg, res, ls)``
@@ -362,6 +363,39 @@ def zero_step(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float,
     wsb = _need_ws(ws)
     _check(lib().zero_step(arr, len(tensors), M, ctypes.byref(h), float(external_sumsq), _ptr(ws), wsb,
                            res.data_ptr(), _stream(stream)), "zero_step")
+
+
+class StepRunner:
+    """A tensor list marshalled once, for a training loop that steps it every
+    iteration: step() and step_amp() call zero_step and zero_step_amp with
+    the pointer tables prepared here, so a call costs one small structure of
+    hyperparameters instead of checking every replica of every tensor again
+    (about 2 ms of host time per call on a 288-tensor list with 8 replicas).
+    The tensors, the workspace and the result record must stay alive and at
+    the same addresses."""
+
+    def __init__(self, tensors: Sequence[ZeroTensor], ws: Optional[torch.Tensor], res: torch.Tensor):
+        _need(res, torch.uint8, "res", RESULT_BYTES)
+        self._arr, self._keep, self.M = _ctensors(tensors, check=True)
+        self._tensors = list(tensors)
+        self.T = len(self._tensors)
+        self.ws, self.res = ws, res
+        self._wsp, self._wsb = _ptr(ws), _need_ws(ws)
+
+    def step(self, hp: HParams, external_sumsq: float = 0.0, stream=None) -> None:
+        h = hp._c()
+        st = lib().zero_step(self._arr, self.T, self.M, ctypes.byref(h), float(external_sumsq), self._wsp, self._wsb,
+                             self.res.data_ptr(), _stream(stream))
+        if st != ZERO_OK:
+            raise ZeroError(st, "zero_step")
+
+    def step_amp(self, hp: HParams, cfg: "LossScaleConfig", ls: torch.Tensor, external_sumsq: float = 0.0,
+                 stream=None) -> None:
+        h, c = hp._c(), cfg._c()
+        st = lib().zero_step_amp(self._arr, self.T, self.M, ctypes.byref(h), ctypes.byref(c), ls.data_ptr(),
+                                 float(external_sumsq), self._wsp, self._wsb, self.res.data_ptr(), _stream(stream))
+        if st != ZERO_OK:
+            raise ZeroError(st, "zero_step_amp")
 
 
 def zero_step_noalloc(tensors: Sequence[ZeroTensor], hp: HParams, external_sumsq: float, res: torch.Tensor,

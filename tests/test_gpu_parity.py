@@ -486,3 +486,36 @@ def test_consecutive_steps_on_one_workspace_each_write_their_record(sizes, M, ma
         assert abs(r["clip_coef"] - ro.clip_coef) <= 1e-9 * ro.clip_coef
     for d, h in zip(dts, state):
         assert_tensor_matches(d, h, "after 5 steps", ulp_max=ulp_gate(*records))
+
+
+def test_step_runner_equals_the_binding_call_bitwise():
+    # the prepared form of zero_step and zero_step_amp (tensor list marshalled
+    # once): three steps with changing hyperparameters, bit for bit against
+    # the plain binding calls on a copy of the same inputs
+    sizes, M = [100_003, 4099, 7], 8
+    case = Case(sizes, M, seed=97)
+    d1, _ = build(case)
+    d2, _ = build(case)
+    r1, r2 = z.new_result(), z.new_result()
+    ws1 = z.workspace(z.zero_step_workspace_bytes(d1, M, z.HParams(max_grad_norm=1.0)))
+    ws2 = z.workspace(z.zero_step_workspace_bytes(d2, M, z.HParams(max_grad_norm=1.0)))
+    runner = z.StepRunner(d1, ws1, r1)
+    for k, hp in enumerate((z.HParams(step=2), z.HParams(step=3, max_grad_norm=0.01), z.HParams(step=4))):
+        runner.step(hp, 0.5 * k)
+        z.zero_step(d2, hp, 0.5 * k, ws2, r2)
+        assert z.read_result(r1) == z.read_result(r2), k
+        for a, b in zip(d1, d2):
+            for x, y in ((a.master, b.master), (a.exp_avg, b.exp_avg), (a.exp_avg_sq, b.exp_avg_sq)):
+                assert bits_equal(to_np_f32(x), to_np_f32(y)), k
+            assert np.array_equal(to_np_u16(a.param_out), to_np_u16(b.param_out)), k
+    cfg = z.LossScaleConfig(initial_scale_power=4, window=2, hysteresis=1, min_scale=1.0)
+    ls1, ls2 = z.new_loss_scale(), z.new_loss_scale()
+    z.zero_loss_scale_init(cfg, ls1)
+    z.zero_loss_scale_init(cfg, ls2)
+    for k in range(3):
+        hp = z.HParams(step=5 + k)
+        runner.step_amp(hp, cfg, ls1)
+        z.zero_step_amp(d2, hp, cfg, ls2, 0.0, ws2, r2)
+        assert z.read_result(r1) == z.read_result(r2) and z.read_loss_scale(ls1) == z.read_loss_scale(ls2), k
+        for a, b in zip(d1, d2):
+            assert bits_equal(to_np_f32(a.master), to_np_f32(b.master)), k
