@@ -96,8 +96,9 @@ def parse():
     p.add_argument("--fused-final", action="store_true",
                    help="--zero2: each bucket's last micro-batch folded and applied in one pass (zero_bucket_step; "
                         "no clipping or skipping), then zero_step_accumulated with no tensors for the record")
-    p.add_argument("--streams", type=int, default=2,
-                   help="--zero2: side streams the bucket reduces alternate over (1: the launch stream)")
+    p.add_argument("--streams", type=int, default=None,
+                   help="--zero2: side streams the buckets alternate over (1: the launch stream; default 2, "
+                        "3 with --fused-final)")
     p.add_argument("--offload", action="store_true",
                    help="the CPU-offloaded step: zero_offload_step with the optimizer state in host memory")
     p.add_argument("--threads", type=int, default=0, help="--offload: host threads (0: the CPU affinity mask)")
@@ -331,7 +332,7 @@ def zero2_line(a, w, tensors) -> dict:
     # buckets are independent (own accumulators, workspace and partial), so a
     # loop that overlaps communication issues them on side streams; bucket b
     # always goes to the same one, which orders its micro-batches
-    NS = max(1, a.streams)
+    NS = max(1, a.streams if a.streams is not None else (3 if a.fused_final else 2))
     side = [torch.cuda.Stream() for _ in range(NS)] if NS > 1 else [stream]
 
     def step(i, ev=None):

@@ -159,7 +159,7 @@ def main():
                 f"algorithmic bytes\n")
         f.write(f"- every fused launch of a step together: {step_b:,.0f} B per step = {step_b / alg_step:.4f} x "
                 f"the step's algorithmic bytes ({alg_step / n:.0f} B x {n:,})\n")
-        f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
+        f.write(f"\nLibrary source hash (kernels and host planner, sha256[:16]): {src_hash()}\n")
     tf_path = os.path.join(profiles, "traffic.json")
     tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
     tf[str(a.workload)] = {"kernel": kshort, "kernel_source_sha256_16": src_hash(),
@@ -293,7 +293,7 @@ def main_zero2(a):
         f.write(f"- WRITE_SIZE over {nw} dispatches -> {write_b:,.0f} B written per step\n")
         f.write(f"- traffic {fetch_b + write_b:,.0f} B per step = {(fetch_b + write_b) / alg[dom]:.4f} x the "
                 f"algorithmic bytes\n")
-        f.write(f"\nKernel source sha256[:16]: {src_hash()}\n")
+        f.write(f"\nLibrary source hash (kernels and host planner, sha256[:16]): {src_hash()}\n")
     tf_path = os.path.join(a.profiles_dir, "traffic.json")
     tf = json.load(open(tf_path)) if os.path.exists(tf_path) else {}
     tf[f"{wi}_zero2_K1" + ("_fused" if fused else "")] = {"kernel": dom, "kernel_source_sha256_16": src_hash(),
