@@ -3,7 +3,8 @@ HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter passes (one
 counter per run), calibrated on a plain device copy of known size.
 
     python bench_profile.py --workload 2 [--steps 10] [--out rocprof_raw]
-    python bench_profile.py --zero2 [--workload 3]     (the ZeRO-2 streaming leg of bench.py)
+    python bench_profile.py --zero2 [--workload 3] [--fused-final]  (the ZeRO-2 streaming leg of bench.py)
+    python bench_profile.py --queues --workload 4      (HBM request latency and credit stalls per kernel)
 
 Needs an MI355X with rocprofv3. Writes:
   profiles/<kernel>_<workload tag>.md   the figures used and the commands that made them
@@ -66,9 +67,14 @@ def main():
     ap.add_argument("--profiles-dir", default="profiles", help="where the summaries go (relative)")
     ap.add_argument("--summarize-only", action="store_true", help="re-read existing raw output, run nothing")
     ap.add_argument("--zero2", action="store_true", help="profile bench.py --zero2 (one micro-batch)")
+    ap.add_argument("--queues", action="store_true",
+                    help="HBM request queues instead: average read and write latency at the L2-fabric interface "
+                         "and DRAM-credit stalls, per kernel of the bench command (two counter passes)")
     ap.add_argument("--fused-final", action="store_true",
                     help="with --zero2: the fused final pass (bench.py --zero2 --fused-final)")
     a = ap.parse_args()
+    if a.queues:
+        return main_queues(a)
     if a.zero2:
         return main_zero2(a)
     sys.path.insert(0, ROOT)
@@ -302,6 +308,63 @@ def main_zero2(a):
                             "rocprof_us_per_step": round(per[dom]["ns"] / 1e3, 2), "fetch_factor": round(f_fetch, 5),
                             "write_factor": round(f_write, 5), "summary": os.path.join("profiles", os.path.basename(md))}
     json.dump(tf, open(tf_path, "w"), indent=1, sort_keys=True)
+    print(open(md).read())
+
+
+QUEUE_PASSES = [
+    ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum"],
+    ["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_BUSY_sum", "GRBM_GUI_ACTIVE"],
+]
+
+
+def main_queues(a):
+    """Why a kernel's bytes move at the rate they do: per fused kernel of the
+    bench command, the read and write requests that leave the L2 for the
+    fabric, their average latency there (requests in flight summed over
+    cycles, over requests), and the share of the L2's busy cycles stalled for
+    DRAM credits. Two counter passes (at most four TCC counters each)."""
+    sys.path.insert(0, ROOT)
+    from synth.workloads import workload
+    w = workload(a.workload)
+    out = os.path.join(a.out, f"w{a.workload}_queues")
+    os.chdir(ROOT)
+    os.makedirs(out, exist_ok=True)
+    bench = ["python", "-u", "bench.py", "--workload", str(a.workload), "--cpu-sample", "0", "--steps",
+             str(a.steps), "--warmup", "2", "--no-skipped-leg"]
+    cmds = {f"pass{i}": ["rocprofv3", "--pmc", *p, "--output-format", "csv", "-d", f"{out}/pass{i}", "-o", "run",
+                         "--"] + bench for i, p in enumerate(QUEUE_PASSES)}
+    if not a.summarize_only:
+        for k, c in cmds.items():
+            run(c, f"{out}/{k}.log")
+    per = {}
+    for k in cmds:
+        for r in csv.DictReader(open(one(f"{out}/{k}/run_counter_collection.csv"))):
+            nm = r["Kernel_Name"]
+            if "fused_kernel" not in nm:
+                continue
+            nm = nm.split("(zero::PlanHeader")[0].replace("void zero::(anonymous namespace)::", "")
+            per.setdefault(nm, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    os.makedirs(a.profiles_dir, exist_ok=True)
+    md = os.path.join(a.profiles_dir, f"hbm_queues_{TAGS[a.workload]}.md")
+    with open(md, "w") as f:
+        f.write(f"# HBM request queues of the step's kernels on {w.name}\n\n")
+        f.write("Commands (repository root, MI355X, ROCm 7.2):\n\n")
+        for c in cmds.values():
+            f.write(f"    {' '.join(c)}\n")
+        f.write("\nPer kernel, averaged over its dispatches. Requests are those the L2 sends to the fabric (reads in "
+                "128 B, writes in 64 B); latency is requests in flight summed over cycles, divided by requests "
+                "(TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ); a credit stall is a cycle the L2 could not send for "
+                "want of DRAM credits, as a share of its busy cycles.\n\n")
+        f.write("| kernel | read requests | write requests | read latency (cycles) | write latency (cycles) | "
+                "read credit stalls | write credit stalls |\n|---|---|---|---|---|---|---|\n")
+        for nm, c in per.items():
+            m = {k: sum(v) / len(v) for k, v in c.items()}
+            rd, wr, busy = m["TCC_EA0_RDREQ_sum"], m["TCC_EA0_WRREQ_sum"], m["TCC_BUSY_sum"]
+            f.write(f"| {nm} | {rd:,.0f} | {wr:,.0f} | {m['TCC_EA0_RDREQ_LEVEL_sum'] / rd:,.0f} | "
+                    f"{(m['TCC_EA0_WRREQ_LEVEL_sum'] / wr if wr else 0):,.0f} | "
+                    f"{m['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / busy:.3f} | "
+                    f"{m['TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum'] / busy:.3f} |\n")
+        f.write(f"\nLibrary source hash (kernels and host planner, sha256[:16]): {src_hash()}\n")
     print(open(md).read())
 
 

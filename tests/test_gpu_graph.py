@@ -143,3 +143,65 @@ def test_captured_zero2_step_replays_like_eager_calls():
             assert bits_equal(to_np_f32(a), to_np_f32(b)), f"replay {k} accumulator"
         re, rg = z.read_result(sides[0][6]), z.read_result(sides[1][6])
         assert re == rg and rg["status"] == 0, (k, re, rg)
+
+
+@pytest.mark.parametrize("max_norm", [0.0, 0.05])
+def test_captured_noalloc_step_replays_like_eager_calls(max_norm):
+    # zero_step_noalloc (the plan in the library's static scratch) captured
+    # after one eager warm-up call, replayed against zero_step with a caller
+    # workspace made eagerly on a twin
+    M = 4
+    case = Case([100_003, 4099, 512, 1], M, seed=730)
+    d_eager, _ = build(case)
+    d_graph, _ = build(case)
+    hp = z.HParams(step=8, max_grad_norm=max_norm)
+    ws_e = z.workspace(z.zero_step_workspace_bytes(d_eager, M, hp))
+    res_e, res_g = z.new_result(), z.new_result()
+    z.zero_step(d_eager, hp, 0.0, ws_e, res_e)
+    z.zero_step_noalloc(d_graph, hp, 0.0, res_g)  # warm-up: the plan reaches the scratch outside the graph
+    torch.cuda.synchronize()
+    same_state(d_eager, d_graph, "warm-up")
+    g = capture(lambda: z.zero_step_noalloc(d_graph, hp, 0.0, res_g))
+    for k in range(REPLAYS):
+        g.replay()
+        z.zero_step(d_eager, hp, 0.0, ws_e, res_e)
+        eager_work()
+        same_state(d_eager, d_graph, f"replay {k}")
+        re, rg = z.read_result(res_e), z.read_result(res_g)
+        assert re == rg and rg["status"] == 0, (k, re, rg)
+
+
+def test_captured_fused_bucket_pass_replays_like_eager_calls():
+    # a bucket's fused final pass and the record from its partial, captured
+    # together, against the same two calls made eagerly on a twin
+    M = 8
+    case = Case([70_001, 4099], M, seed=740)
+    d_eager, _ = build(case)
+    d_graph, _ = build(case)
+    hp = z.HParams(step=12)
+    parts_e, parts_g = z.new_bucket_partials(1), z.new_bucket_partials(1)
+    se = z.BucketStepper([z.BucketTensor(d.grads, None, d.master, d.exp_avg, d.exp_avg_sq, d.param_out)
+                          for d in d_eager], parts_e)
+    sg = z.BucketStepper([z.BucketTensor(d.grads, None, d.master, d.exp_avg, d.exp_avg_sq, d.param_out)
+                          for d in d_graph], parts_g)
+    res_e, res_g = z.new_result(), z.new_result()
+
+    def eager():
+        se.step(0, hp, 33)
+        z.zero_step_accumulated([], hp, parts_e, 1, 33, 0.0, None, res_e)
+
+    def graphed():
+        sg.step(0, hp, 33)
+        z.zero_step_accumulated([], hp, parts_g, 1, 33, 0.0, None, res_g)
+
+    eager()
+    graphed()  # warm-up: the bucket's plan is uploaded outside the graph
+    torch.cuda.synchronize()
+    g = capture(graphed)
+    for k in range(REPLAYS):
+        g.replay()
+        eager()
+        eager_work()
+        same_state(d_eager, d_graph, f"replay {k}")
+        re, rg = z.read_result(res_e), z.read_result(res_g)
+        assert re == rg and rg["status"] == 0, (k, re, rg)
