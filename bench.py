@@ -333,6 +333,9 @@ def zero2_line(a, w, tensors) -> dict:
     # loop that overlaps communication issues them on side streams; bucket b
     # always goes to the same one, which orders its micro-batches
     NS = max(1, a.streams if a.streams is not None else (3 if a.fused_final else 2))
+    # the step's buckets together write more than the Infinity Cache holds:
+    # their state stores stream out (zero_step decides this by itself)
+    stream_flag = z.BUCKET_STREAM_STORES if n > z.STREAM_STORES_MIN_PARAMS else 0
     side = [torch.cuda.Stream() for _ in range(NS)] if NS > 1 else [stream]
 
     def step(i, ev=None):
@@ -344,7 +347,7 @@ def zero2_line(a, w, tensors) -> dict:
         for k in range(K):
             if fused and k == K - 1:
                 for b, sp in enumerate(steppers):
-                    sp.step(z.BUCKET_ACCUMULATE if k else 0, hp, stamp, side[b % NS])
+                    sp.step((z.BUCKET_ACCUMULATE if k else 0) | stream_flag, hp, stamp, side[b % NS])
                 continue
             flags = (z.BUCKET_ACCUMULATE if k else 0) | (z.BUCKET_FINAL if k == K - 1 else 0)
             for b, rd in enumerate(reducers):

@@ -190,6 +190,9 @@ size_t zero_step_workspace_bytes(const zero_tensor* tensors, int32_t T, int32_t 
  * The norm and found_inf are global over all T tensors. Without clipping and
  * skipping it is one streaming pass; with either, a first pass writes the fp32
  * reduced gradient to the workspace and a second pass applies the update.
+ * Above ZERO_STREAM_STORES_MIN_PARAMS parameters in all the call's tensors
+ * together, the state stores of the updating pass stream out to memory (see
+ * ZERO_BUCKET_STREAM_STORES); the results do not depend on it.
  * ws: device workspace of zero_step_workspace_bytes(...) bytes, 256-byte
  * aligned. The workspace caches the tensor table of the call; it belongs to
  * the library from this call until the caller reuses it for anything else,
@@ -330,6 +333,15 @@ int zero_step_amp(const zero_tensor* tensors, int32_t T, int32_t M, const zero_a
 /* flags of zero_bucket_reduce */
 #define ZERO_BUCKET_ACCUMULATE 1 /* add the fold to acc; otherwise store it (first micro-batch) */
 #define ZERO_BUCKET_FINAL 2      /* last micro-batch of the step: also write the bucket partial */
+/* flag of zero_bucket_step: the state stores of the pass stream out to memory
+ * (non-temporal, system scope) instead of waiting in the caches. Results are
+ * the same either way; it is faster when the step's buckets together write
+ * more than the GPU's 256 MiB Infinity Cache holds, i.e. above
+ * ZERO_STREAM_STORES_MIN_PARAMS parameters (12 bytes of state and 2 of bf16
+ * output each), and slower below. zero_step and zero_step_accumulated make
+ * this choice themselves from the size of the step. */
+#define ZERO_BUCKET_STREAM_STORES 4
+#define ZERO_STREAM_STORES_MIN_PARAMS ((256ll << 20) / 14)
 
 /* One tensor shard of a gradient bucket. Host memory. */
 typedef struct zero_grad_shard {
@@ -411,9 +423,10 @@ size_t zero_step_accumulated_workspace_bytes(const zero_acc_tensor* tensors, int
  * coefficient, skip, as zero_step); unless skipped, AdamW and the bf16 emit
  * are applied to every tensor from g = acc * fl32(hp->grad_scale). A partial
  * with another stamp or scale sets res_dev->status = ZERO_ERR_BUCKET_PARTIALS
- * and nothing is written. ws: device workspace of
- * zero_step_accumulated_workspace_bytes(...) bytes, 256-byte aligned, as for
- * zero_step.
+ * and nothing is written. The state stores stream out above
+ * ZERO_STREAM_STORES_MIN_PARAMS parameters, as in zero_step. ws: device
+ * workspace of zero_step_accumulated_workspace_bytes(...) bytes, 256-byte
+ * aligned, as for zero_step.
  */
 int zero_step_accumulated(const zero_acc_tensor* tensors, int32_t T, const zero_adamw_hparams* hp,
                           const zero_bucket_partial* partials_dev, int32_t nbuckets, uint64_t stamp,
@@ -477,9 +490,11 @@ size_t zero_bucket_step_workspace_bytes(const zero_bucket_tensor* tensors, int32
 
 /*
  * zero_bucket_step -- the final micro-batch of one bucket (T tensor shards,
- * M bf16 replicas each), folded, added to the accumulator when `flags` is
- * ZERO_BUCKET_ACCUMULATE (0: the bucket's only micro-batch; any other bit is
- * an error), scaled and applied with AdamW and the bf16 emit in one pass;
+ * M bf16 replicas each), folded, added to the accumulator when `flags` has
+ * ZERO_BUCKET_ACCUMULATE (without it: the bucket's only micro-batch), scaled
+ * and applied with AdamW and the bf16 emit in one pass, its state stores
+ * streamed when `flags` has ZERO_BUCKET_STREAM_STORES (any other bit is an
+ * error);
  * the bucket partial *partial_dev (device, 32 bytes) gets the bucket's sum of
  * squares and flag with `stamp` and fl32(hp->grad_scale). hp must have
  * max_grad_norm <= 0 and skip_on_nonfinite == 0 (otherwise

@@ -61,6 +61,9 @@ NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 RESULT_BYTES = 32
 BUCKET_ACCUMULATE = 1
 BUCKET_FINAL = 2
+BUCKET_STREAM_STORES = 4
+# steps above this many parameters write more than the 256 MiB Infinity Cache holds
+STREAM_STORES_MIN_PARAMS = (256 << 20) // 14
 BUCKET_PARTIAL_BYTES = 32
 
 # Every symbol the C ABI exports (include/zero_step.h).

@@ -451,6 +451,7 @@ int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     fin.skip = skip;
     fin.ls = ls;
     fin.scale_from = ls;
+    fin.stream = !two_pass && stream_state_stores(total_n);
     if (amp) fin.lscfg = *lscfg;
     hipError_t e = launch_fused(first_mode, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
                                 gscale, c, plan.parts, fin, nullptr, stream);
@@ -458,6 +459,7 @@ int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     if (two_pass) {
         // the stored gradient is already scaled
         FinalizeArgs none{};
+        none.stream = stream_state_stores(total_n);
         e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, M, 1.0f,
                          c, plan.parts, none, res_dev, stream);
         if (e != hipSuccess) return ZERO_ERR_HIP;
@@ -751,6 +753,7 @@ static int acc_step_impl(const zero_acc_tensor* tensors, int32_t T, const zero_a
         if (e != hipSuccess) return ZERO_ERR_HIP;
         FinalizeArgs fin{};
         fin.scale_from = ls;
+        fin.stream = stream_state_stores(total_n);
         e = launch_fused(Mode::PassB, plan.geom[1], plan.hdr, plan.desc, plan.map1, plan.tiles[1], plan.sig, 0,
                          gscale, derive(hp), nullptr, fin, res_dev, stream);
     }
@@ -805,7 +808,7 @@ int zero_bucket_step(const zero_bucket_tensor* tensors, int32_t T, int32_t M, in
     // the update cannot wait for the global norm: no clipping, no skipping
     if (!bucket_tensors_ok(tensors, T, M) || !hparams_ok(hp) || partial_dev == nullptr) return ZERO_ERR_INVALID_ARGUMENT;
     if (hp->max_grad_norm > 0.0 || hp->skip_on_nonfinite != 0) return ZERO_ERR_INVALID_ARGUMENT;
-    if ((flags & ~ZERO_BUCKET_ACCUMULATE) != 0) return ZERO_ERR_INVALID_ARGUMENT;
+    if ((flags & ~(ZERO_BUCKET_ACCUMULATE | ZERO_BUCKET_STREAM_STORES)) != 0) return ZERO_ERR_INVALID_ARGUMENT;
     const bool accumulate = (flags & ZERO_BUCKET_ACCUMULATE) != 0;
     int64_t total_n = 0;
     std::vector<PlanTensor> pts(static_cast<size_t>(T));
@@ -833,6 +836,7 @@ int zero_bucket_step(const zero_bucket_tensor* tensors, int32_t T, int32_t M, in
     fin.stamp = stamp;
     fin.accumulate = accumulate ? 1 : 0;
     fin.final = 1;
+    fin.stream = (flags & ZERO_BUCKET_STREAM_STORES) != 0;
     return hip_status(launch_fused(Mode::BucketFull, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0],
                                    plan.sig, M, gscale, derive(hp), plan.parts, fin, nullptr, stream));
 }

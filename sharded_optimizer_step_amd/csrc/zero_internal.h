@@ -136,7 +136,16 @@ struct FinalizeArgs {
     uint64_t stamp;
     int accumulate;                // add the fold to the accumulator
     int final;                     // last micro-batch: norm partials into *slot
+    int stream;                    // the single pass's state stores stream past the caches (stream_state_stores)
 };
+
+// The Infinity Cache of an MI355X (256 MiB) takes a step's state writes and
+// writes them back later. When a step writes more than it holds, those
+// write-backs fall among the step's own reads, and state stores that go out to
+// memory as they are written are faster; when the writes fit, keeping them is
+// faster. The choice is made per step from what it writes: 12 bytes of state
+// and 2 of bf16 output per parameter.
+inline bool stream_state_stores(int64_t n) { return n > ZERO_STREAM_STORES_MIN_PARAMS; }
 
 // Byte offsets of the regions of a zero_step workspace.
 struct PlanOffsets {

@@ -49,6 +49,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ helpers
 
@@ -274,6 +275,7 @@ struct Scal {
     bool last;        // Reduce: this pass ends the fold
     bool accumulate;  // Acc: add the fold to the accumulator (else store it)
     bool final;       // Acc: also check and square g = acc * gscale
+    bool stream;      // Full at 16 vectors per thread, Adam: state stores stream past the caches
 };
 
 // One element, scalar path. PREADD (Full only): when k.accumulate, the fold
@@ -373,6 +375,79 @@ __device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamSca
                                       const float (&g)[8])
 {
     adam8_from(x, k, c, e0, g, load_state8(x, e0));
+}
+
+// ------------------------------------------------------------------ whole-line state I/O
+//
+// The paired update of the 16-vector geometries works on half vectors: lane l
+// of a wave takes elements 4l..4l+3 (half A) and 256+4l..256+4l+3 (half B) of
+// the wave's 512-element block, so that each state load or store instruction
+// of the wave covers 1 KiB of whole 128-byte lines (with 8 consecutive
+// elements per lane, two instructions each write half of every line).
+
+// Store 16 bytes at byte offset `off` of the 512-element fp32 block that
+// starts at `blk` (the same address in every lane of the wave), as a buffer
+// store whose range is that block. STREAM: with the non-temporal and
+// system-scope cache-policy bits (nt, sc1), so that the lines go out to
+// memory in the order they are written instead of waiting, dirty, in the
+// caches; otherwise a plain store.
+template <bool STREAM>
+__device__ __forceinline__ void st_line(float* blk, uint32_t off, f32x4 v)
+{
+    constexpr int kNt = 2, kSc1 = 16;  // CDNA3/CDNA4 buffer cache-policy bits
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(blk), 0, 2048, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, static_cast<int>(off), 0,
+                                           STREAM ? (kNt | kSc1) : 0);
+}
+
+__device__ __forceinline__ void st_nt2(uint16_t* p, u32x2 v) { __builtin_nontemporal_store(v, (ZERO_GLOBAL u32x2*)p); }
+
+// The state of the lane's two halves of the block at element `blk` (uniform
+// over the wave); a half that is not valid reads the block's first element.
+__device__ __forceinline__ State8 load_halves(const Ctx& x, int64_t blk, int lane, bool oa, bool ob)
+{
+    const int64_t a = oa ? blk + 4 * lane : blk, b = ob ? blk + 256 + 4 * lane : blk;
+    State8 q;
+    q.w0 = ld4(x.master + a);
+    q.w1 = ld4(x.master + b);
+    q.m0 = ld4(x.m + a);
+    q.m1 = ld4(x.m + b);
+    q.v0 = ld4(x.v + a);
+    q.v1 = ld4(x.v + b);
+    return q;
+}
+
+// The lane's 4-element half at byte offset `off` of the block at `blk`, as
+// four fp32 stores of master, m and v and the bf16 output.
+template <bool STREAM>
+__device__ __forceinline__ void store_half(const Ctx& x, int64_t blk, uint32_t off, const float* w, const float* m,
+                                           const float* v)
+{
+    st_line<STREAM>(x.master + blk, off, f32x4{w[0], w[1], w[2], w[3]});
+    st_line<STREAM>(x.m + blk, off, f32x4{m[0], m[1], m[2], m[3]});
+    st_line<STREAM>(x.v + blk, off, f32x4{v[0], v[1], v[2], v[3]});
+    st_nt2(x.out + blk + off / 4u,
+           u32x2{bf16_rne(w[0]) | (bf16_rne(w[1]) << 16), bf16_rne(w[2]) | (bf16_rne(w[3]) << 16)});
+}
+
+// AdamW + bf16 emit of the lane's two halves (g[0..3]: half A, g[4..7]: half
+// B) from their state q; a half is stored only when valid.
+__device__ __forceinline__ void adam_halves(const Ctx& x, const Scal& k, const AdamScalars& c, int64_t blk, int lane,
+                                            bool oa, bool ob, const float (&g)[8], const State8& q)
+{
+    float w[8] = {q.w0.x, q.w0.y, q.w0.z, q.w0.w, q.w1.x, q.w1.y, q.w1.z, q.w1.w};
+    float m[8] = {q.m0.x, q.m0.y, q.m0.z, q.m0.w, q.m1.x, q.m1.y, q.m1.z, q.m1.w};
+    float v[8] = {q.v0.x, q.v0.y, q.v0.z, q.v0.w, q.v1.x, q.v1.y, q.v1.z, q.v1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) adam1(g[j], k.coef, c, w[j], m[j], v[j]);
+    const uint32_t off = 16u * static_cast<uint32_t>(lane);
+    if (k.stream) {
+        if (oa) store_half<true>(x, blk, off, w, m, v);
+        if (ob) store_half<true>(x, blk, off + 1024u, w + 4, m + 4, v + 4);
+    } else {
+        if (oa) store_half<false>(x, blk, off, w, m, v);
+        if (ob) store_half<false>(x, blk, off + 1024u, w + 4, m + 4, v + 4);
+    }
 }
 
 // Eight elements [e0, e0+8), 16-byte vector path.
@@ -519,46 +594,84 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
         }
         bool paired = false;
         if constexpr (OP == Op::Full && U == 16) {
-            // The update in pairs of vectors: both states are loaded, then
-            // both vectors are updated, which halves the dependent round
-            // trips of the update. A lane past the shard's last vector loads
-            // the shard's first vector (it exists: nvec > 0) and stores
-            // nothing, so the loads take no per-lane branch; the scheduling
-            // barriers keep each pair's loads together, ahead of its
-            // arithmetic. (The 1024-thread geometries run four waves per
-            // SIMD, within 128 registers, where a second state does not fit.)
+            // The update in pairs of vectors, on half vectors (whole-line
+            // state I/O above): the fold's sums are first moved across lanes
+            // so that lane l holds elements 4l..4l+3 and 256+4l..256+4l+3 of
+            // each of its wave's 512-element blocks; both vectors' state is
+            // loaded, then both are updated, which halves the dependent round
+            // trips of the update. A half past the shard's last vector loads
+            // the block's first element and stores nothing, so the loads take
+            // no per-lane branch; the scheduling barriers keep each pair's
+            // loads together, ahead of its arithmetic. (The 1024-thread
+            // geometries run four waves per SIMD, within 128 registers, where
+            // a second state does not fit.)
             paired = x.nvec > 0;
             if (paired) {
+                const int64_t vb = t * kTileVecs + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(wave)) * 64 * U;
+                const int srcA = lane >> 1, srcB = 32 + (lane >> 1);
+                const bool odd = (lane & 1) != 0;
 #pragma unroll
                 for (int u = 0; u < U; u += 2) {
-                    const State8 qa = load_state8(x, x.head + (ok[u] ? v0 + u * 64 : 0) * kVec);
-                    const State8 qb = load_state8(x, x.head + (ok[u + 1] ? v0 + (u + 1) * 64 : 0) * kVec);
+                    bool oa[2], ob[2];
+                    int64_t blk[2];
+                    State8 q[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t vv = vb + (u + h) * 64;  // the block's first vector
+                        oa[h] = vv + (lane >> 1) < x.nvec;
+                        ob[h] = vv + 32 + (lane >> 1) < x.nvec;
+                        blk[h] = x.head + (vv < x.nvec ? vv : 0) * kVec;
+                        q[h] = load_halves(x, blk[h], lane, oa[h], ob[h]);
+                    }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        // element 4l+j of the block sits in lane l/2, slot
+                        // 4(l%2)+j; element 256+4l+j in lane 32+l/2
+                        float nw[8];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float a0 = __shfl(s[u + h][j], srcA, 64), a1 = __shfl(s[u + h][4 + j], srcA, 64);
+                            const float b0 = __shfl(s[u + h][j], srcB, 64), b1 = __shfl(s[u + h][4 + j], srcB, 64);
+                            nw[j] = odd ? a1 : a0;
+                            nw[4 + j] = odd ? b1 : b0;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) s[u + h][j] = nw[j];
+                    }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        if (ok[u + h]) {
+                        if (oa[h] || ob[h]) {
                             float g[8];
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) {
-                                g[j] = s[u + h][j] * k.gscale;
-                                bad |= nonfinite(g[j]);
-                                const double d = static_cast<double>(g[j]);
-                                acc = fma(d, d, acc);
+                            for (int j = 0; j < 8; ++j) g[j] = s[u + h][j] * k.gscale;
+                            if (oa[h]) {
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    bad |= nonfinite(g[j]);
+                                    const double d = static_cast<double>(g[j]);
+                                    acc = fma(d, d, acc);
+                                }
                             }
-                            adam8_from(x, k, c, x.head + (v0 + (u + h) * 64) * kVec, g, h == 0 ? qa : qb);
+                            if (ob[h]) {
+#pragma unroll
+                                for (int j = 4; j < 8; ++j) {
+                                    bad |= nonfinite(g[j]);
+                                    const double d = static_cast<double>(g[j]);
+                                    acc = fma(d, d, acc);
+                                }
+                            }
+                            adam_halves(x, k, c, blk[h], lane, oa[h], ob[h], g, q[h]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
         }
-        // Every other pass and geometry takes the per-vector loop, and so does
-        // a tile with no whole vector (only its scalar head and tail to do).
-        // In the paired kernels the loop thus never finds a vector to update,
-        // yet it is compiled into them on purpose: with it the registers are
-        // allocated differently (241 against 224 VGPRs) and the 64-replica
-        // step measured 0.5-0.75% faster, on four boxes, than without it.
-        if (!paired) {
+        // Every other pass and geometry takes the per-vector loop (in the
+        // paired kernels a tile with no whole vector has only its scalar head
+        // and tail to do).
+        if (!(OP == Op::Full && U == 16) && !paired) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!ok[u]) continue;
@@ -605,16 +718,19 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
         }
     } else {
         static_assert(OP == Op::Adam, "fused tiles fold, or update from the stored gradient");
+        // on half vectors, like the paired update: whole-line state I/O
+        const int64_t vw = t * kTileVecs + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(wave)) * 64 * U;
 #pragma unroll 1
         for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + u * 64;
-            if (v < x.nvec) {
-                const int64_t e0 = x.head + v * kVec;
-                const f32x4 a = ld4(x.gin + e0), b = ld4(x.gin + e0 + 4);
-                const float g[8] = {a.x * k.gscale, a.y * k.gscale, a.z * k.gscale, a.w * k.gscale,
-                                    b.x * k.gscale, b.y * k.gscale, b.z * k.gscale, b.w * k.gscale};
-                adam8(x, k, c, e0, g);
-            }
+            const int64_t vv = vw + u * 64;  // the block's first vector
+            if (vv >= x.nvec) break;
+            const bool oa = vv + (lane >> 1) < x.nvec, ob = vv + 32 + (lane >> 1) < x.nvec;
+            const int64_t blk = x.head + vv * kVec;
+            const f32x4 a = ld4(x.gin + (oa ? blk + 4 * lane : blk)), b = ld4(x.gin + (ob ? blk + 256 + 4 * lane : blk));
+            const State8 q = load_halves(x, blk, lane, oa, ob);
+            const float g[8] = {a.x * k.gscale, a.y * k.gscale, a.z * k.gscale, a.w * k.gscale,
+                                b.x * k.gscale, b.y * k.gscale, b.z * k.gscale, b.w * k.gscale};
+            adam_halves(x, k, c, blk, lane, oa, ob, g, q);
         }
     }
     if (t == 0 && tid < x.head) do_one<OP, 0, true, PREADD>(x, k, c, tid, acc, bad);
@@ -829,7 +945,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(const PlanHeader* __restrict_
                       : MODE == Mode::PassA                          ? Op::PassA
                       : MODE == Mode::Acc                            ? Op::Acc
                                                                      : Op::Adam;
-    const Scal k{gscale, coef, false, fin.accumulate != 0, fin.final != 0};
+    const Scal k{gscale, coef, false, fin.accumulate != 0, fin.final != 0, fin.stream != 0};
     double acc = 0.0;
     uint32_t bad = 0;
     const TileRef tr = map[blockIdx.x];

@@ -63,6 +63,12 @@ def test_struct_layouts_match_header(tmp_path):
     body.append('printf("zero_bucket_partial %zu\\n", sizeof(zero_bucket_partial));')
     for f in ("sumsq", "stamp", "found_inf", "grad_scale", "reserved"):
         body.append(f'printf("zero_bucket_partial.{f} %zu\\n", offsetof(zero_bucket_partial, {f}));')
+    consts = {"ZERO_BUCKET_ACCUMULATE": z.BUCKET_ACCUMULATE, "ZERO_BUCKET_FINAL": z.BUCKET_FINAL,
+              "ZERO_BUCKET_STREAM_STORES": z.BUCKET_STREAM_STORES,
+              "ZERO_STREAM_STORES_MIN_PARAMS": z.STREAM_STORES_MIN_PARAMS,
+              "ZERO_NOALLOC_SCRATCH_BYTES": z.NOALLOC_SCRATCH_BYTES}
+    for cname in consts:
+        body.append(f'printf("{cname} %lld\\n", (long long)({cname}));')
     src = tmp_path / "layout.c"
     src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"zero_step.h\"\nint main(void){" +
                    "".join(body) + "return 0;}\n")
@@ -75,6 +81,8 @@ def test_struct_layouts_match_header(tmp_path):
         assert int(got[cname]) == ctypes.sizeof(cls), cname
         for f, _ in cls._fields_:
             assert int(got[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+    for cname, v in consts.items():
+        assert int(got[cname]) == v, cname
     assert int(got["zero_result"]) == z.RESULT_BYTES
     # read_loss_scale unpacks "<ffii"
     assert int(got["zero_loss_scale"]) == z.LOSS_SCALE_BYTES
@@ -455,6 +463,9 @@ def test_bucket_step_argument_checks():
     assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(_hp(max_grad_norm=1.0)), 1, part, ws, need, None) == 1
     assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(_hp(skip_on_nonfinite=1)), 1, part, ws, need, None) == 1
     assert L.zero_bucket_step(arr, 1, M, z.BUCKET_FINAL, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, 8, ctypes.byref(ok), 1, part, ws, need, None) == 1
+    assert L.zero_bucket_step(arr, 1, M, z.BUCKET_STREAM_STORES | z.BUCKET_FINAL, ctypes.byref(ok), 1, part, ws, need,
+                              None) == 1
     assert L.zero_bucket_step(arr, 1, M, z.BUCKET_ACCUMULATE, ctypes.byref(ok), 1, part, ws, need, None) == 1
     assert L.zero_bucket_step(arr, 1, M, 0, ctypes.byref(ok), 1, None, ws, need, None) == 1
     assert L.zero_bucket_step(arr, 1, 0, 0, ctypes.byref(ok), 1, part, ws, need, None) == 1

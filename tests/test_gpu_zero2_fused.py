@@ -62,7 +62,7 @@ def _state(dts):
              to_np_f32(d.exp_avg_sq).view(np.uint32), to_np_u16(d.param_out)) for d in dts]
 
 
-def run_both(sizes, M, K, buckets, hp, seed, offs=None, inject=None):
+def run_both(sizes, M, K, buckets, hp, seed, offs=None, inject=None, extra_flags=0):
     """K micro-batches of every bucket through (1) zero_bucket_reduce for the
     first K-1 and zero_bucket_step for the last, and (2) zero_bucket_reduce
     for all K then zero_step_accumulated, on two copies of the same state.
@@ -102,7 +102,7 @@ def run_both(sizes, M, K, buckets, hp, seed, offs=None, inject=None):
                     acc_before = [to_np_f32(a).copy() for a in acc1]
                 bts = [z.BucketTensor(dev[t], acc1[t] if k else None, d1[t].master, d1[t].exp_avg,
                                       d1[t].exp_avg_sq, d1[t].param_out) for t in idx]
-                z.zero_bucket_step(bts, A if k else 0, hp, stamp, p1[32 * b:32 * b + 32],
+                z.zero_bucket_step(bts, (A if k else 0) | extra_flags, hp, stamp, p1[32 * b:32 * b + 32],
                                    z.workspace(z.zero_bucket_step_workspace_bytes(bts, M)))
         want = [oracle.grad_accumulate(host[t], want[t] if k else None) for t in range(len(sizes))]
     r1, r2 = z.new_result(), z.new_result()
@@ -144,6 +144,29 @@ def test_fused_final_pass_matches_the_oracle_and_the_two_pass_form(sizes, M, K, 
     for a, b in zip(acc1, acc_before):  # the fused pass reads the accumulator and leaves it as it was
         assert bits_equal(to_np_f32(a), b)
     print(where, st)
+
+
+@pytest.mark.parametrize("sizes,M,K,buckets", [
+    ([8_400_000, 4099], 8, 2, [[0], [1]]),   # 256 x 16, paired update, a half-filled last block
+    ([8_400_000, 70_001], 20, 1, [[1, 0]]),  # 512 x 16
+    ([70_001, 5, 4099], 4, 2, [[0, 1, 2]]),  # too few tiles for 16 vectors per thread: the per-vector path
+])
+def test_fused_final_pass_with_streamed_state_stores(sizes, M, K, buckets):
+    # ZERO_BUCKET_STREAM_STORES changes only the cache policy of the state
+    # stores: the state stays bit-identical to the two-pass form's
+    hp = z.HParams(step=9, grad_scale=0.5)
+    r1, r2, d1, d2, acc1, acc_before, new, ro = run_both(sizes, M, K, buckets, hp, seed=640 + M,
+                                                         extra_flags=z.BUCKET_STREAM_STORES)
+    where = f"sizes {sizes}, M {M}, K {K}, streamed"
+    assert r1["status"] == 0 and r1["found_inf"] == ro.found_inf == 0
+    assert math.isclose(r1["sumsq"], r2["sumsq"], rel_tol=1e-12), (where, r1, r2)
+    for t, (a, b) in enumerate(zip(_state(d1), _state(d2))):
+        for x, y, nm in zip(a, b, ("master", "exp_avg", "exp_avg_sq", "param_out")):
+            assert np.array_equal(x, y), f"{where}: tensor {t} {nm} differs from the two-pass form"
+    for t, (d, h) in enumerate(zip(d1, new)):
+        assert_state_matches(to_np_f32(d.master), to_np_f32(d.exp_avg), to_np_f32(d.exp_avg_sq),
+                             to_np_u16(d.param_out), h.master, h.exp_avg, h.exp_avg_sq, h.param_out,
+                             f"{where} t{t}")
 
 
 @pytest.mark.parametrize("offs", [

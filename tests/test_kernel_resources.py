@@ -7,7 +7,7 @@ single-pass kernels with 16 vectors per thread -- which update their state
 two vectors at a time -- must keep two waves per SIMD: the 512-thread
 workgroup needs it to launch at all, and the 256-thread one to put two
 workgroups on a CU. Their register count is pinned to the allocation whose
-speed was measured (241 VGPRs): a compiler or source change that moves it
+speed was measured (230 VGPRs): a compiler or source change that moves it
 fails here, to be measured again, instead of changing the kernel's speed
 silently."""
 import os
@@ -19,7 +19,7 @@ import pytest
 
 from sharded_optimizer_step_amd import _build
 
-PINNED_VGPRS = {("0", "512", "16"): 241, ("0", "256", "16"): 241}
+PINNED_VGPRS = {("0", "512", "16"): 230, ("0", "256", "16"): 230}
 
 
 def remarks():
