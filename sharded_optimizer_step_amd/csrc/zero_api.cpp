@@ -451,7 +451,7 @@ int step_impl(const zero_tensor* tensors, int32_t T, int32_t M, const zero_adamw
     fin.skip = skip;
     fin.ls = ls;
     fin.scale_from = ls;
-    fin.stream = !two_pass && stream_state_stores(total_n);
+    fin.stream = stream_state_stores(total_n);
     if (amp) fin.lscfg = *lscfg;
     hipError_t e = launch_fused(first_mode, plan.geom[0], plan.hdr, plan.desc, plan.map0, plan.tiles[0], plan.sig, M,
                                 gscale, c, plan.parts, fin, nullptr, stream);

@@ -275,7 +275,7 @@ struct Scal {
     bool last;        // Reduce: this pass ends the fold
     bool accumulate;  // Acc: add the fold to the accumulator (else store it)
     bool final;       // Acc: also check and square g = acc * gscale
-    bool stream;      // Full at 16 vectors per thread, Adam: state stores stream past the caches
+    bool stream;      // 16-vector Full and PassA, Adam: whole-line stores stream past the caches
 };
 
 // One element, scalar path. PREADD (Full only): when k.accumulate, the fold
@@ -668,10 +668,55 @@ __device__ __forceinline__ void big_tile(const Ctx& x, const Scal& k, const Adam
                 }
             }
         }
+        if constexpr (OP == Op::PassA && U == 16) {
+            // the first pass of a two-pass step stores its fp32 gradient on
+            // half vectors too: whole lines, streamed as the state stores are
+            if (x.nvec > 0) {
+                const int64_t vb = t * kTileVecs + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(wave)) * 64 * U;
+                const int srcA = lane >> 1, srcB = 32 + (lane >> 1);
+                const bool odd = (lane & 1) != 0;
+                const uint32_t off = 16u * static_cast<uint32_t>(lane);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t vv = vb + u * 64;  // the block's first vector
+                    const bool oa = vv + (lane >> 1) < x.nvec, ob = vv + 32 + (lane >> 1) < x.nvec;
+                    const int64_t blk = x.head + (vv < x.nvec ? vv : 0) * kVec;
+                    float g[8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float a0 = __shfl(s[u][j], srcA, 64), a1 = __shfl(s[u][4 + j], srcA, 64);
+                        const float b0 = __shfl(s[u][j], srcB, 64), b1 = __shfl(s[u][4 + j], srcB, 64);
+                        g[j] = (odd ? a1 : a0) * k.gscale;
+                        g[4 + j] = (odd ? b1 : b0) * k.gscale;
+                    }
+                    if (oa) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            bad |= nonfinite(g[j]);
+                            const double d = static_cast<double>(g[j]);
+                            acc = fma(d, d, acc);
+                        }
+                        const f32x4 ga = {g[0], g[1], g[2], g[3]};
+                        if (k.stream) st_line<true>(x.gout + blk, off, ga); else st_line<false>(x.gout + blk, off, ga);
+                    }
+                    if (ob) {
+#pragma unroll
+                        for (int j = 4; j < 8; ++j) {
+                            bad |= nonfinite(g[j]);
+                            const double d = static_cast<double>(g[j]);
+                            acc = fma(d, d, acc);
+                        }
+                        const f32x4 gb = {g[4], g[5], g[6], g[7]};
+                        if (k.stream) st_line<true>(x.gout + blk, off + 1024u, gb);
+                        else st_line<false>(x.gout + blk, off + 1024u, gb);
+                    }
+                }
+            }
+        }
         // Every other pass and geometry takes the per-vector loop (in the
         // paired kernels a tile with no whole vector has only its scalar head
         // and tail to do).
-        if (!(OP == Op::Full && U == 16) && !paired) {
+        if (!(OP == Op::Full && U == 16) && !(OP == Op::PassA && U == 16) && !paired) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!ok[u]) continue;
