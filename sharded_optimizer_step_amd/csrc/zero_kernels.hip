@@ -379,11 +379,12 @@ __device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamSca
 
 // ------------------------------------------------------------------ whole-line state I/O
 //
-// The paired update of the 16-vector geometries works on half vectors: lane l
-// of a wave takes elements 4l..4l+3 (half A) and 256+4l..256+4l+3 (half B) of
-// the wave's 512-element block, so that each state load or store instruction
-// of the wave covers 1 KiB of whole 128-byte lines (with 8 consecutive
-// elements per lane, two instructions each write half of every line).
+// The paired update of the 16-vector geometries, the update pass and the
+// first pass's gradient stores work on half vectors: lane l of a wave takes
+// elements 4l..4l+3 (half A) and 256+4l..256+4l+3 (half B) of the wave's
+// 512-element block, so that each fp32 load or store instruction of the wave
+// covers 1 KiB of whole 128-byte lines (with 8 consecutive elements per lane,
+// two instructions each write half of every line).
 
 // Store 16 bytes at byte offset `off` of the 512-element fp32 block that
 // starts at `blk` (the same address in every lane of the wave), as a buffer
@@ -394,6 +395,7 @@ __device__ __forceinline__ void adam8(const Ctx& x, const Scal& k, const AdamSca
 template <bool STREAM>
 __device__ __forceinline__ void st_line(float* blk, uint32_t off, f32x4 v)
 {
+    // word 3 of the resource (0x00020000): a raw, unformatted gfx9 buffer
     constexpr int kNt = 2, kSc1 = 16;  // CDNA3/CDNA4 buffer cache-policy bits
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(blk), 0, 2048, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, static_cast<int>(off), 0,
