@@ -268,6 +268,28 @@ def test_zero_step_two_pass_with_many_tiles_per_cu():
     print(st)
 
 
+@pytest.mark.parametrize("extra", [-1, 1])
+def test_zero_step_at_the_stream_threshold(extra):
+    # One parameter below and one above ZERO_STREAM_STORES_MIN_PARAMS: plain
+    # and streamed whole-line state stores in the single pass (256 x 16,
+    # paired update), with a second tensor that ends inside a 512-element
+    # block and a third with a scalar head and tail; every element checked
+    M = 3
+    n = z.STREAM_STORES_MIN_PARAMS + extra
+    sizes = [n - 70_003 - 4099, 70_003, 4099]
+    offs = [[0] * (M + 4), [0] * (M + 4), [3] * (M + 4)]
+    case = Case(sizes, M, seed=66 + extra, offsets=offs)
+    dts, hts = build(case)
+    r, _ = run_step(dts, HP_SINGLE)
+    new, ro = oracle.zero_step(hts, hp_oracle(HP_SINGLE))
+    st = Stats()
+    for i, (d, h) in enumerate(zip(dts, new)):
+        assert_tensor_matches(d, h, f"n {n} tensor {i}", st)
+    assert r["found_inf"] == 0 and r["skipped"] == 0 and r["status"] == 0
+    assert abs(r["grad_norm"] - ro.grad_norm) <= 1e-5 * ro.grad_norm
+    print(f"n={n}", st)
+
+
 def test_zero_step_ragged_unaligned_bucket():
     sizes = [512, 0, 1, 7, 8, 4099, 11_011, 4097, 2048, 2047, 2049, 300_001]
     M = 4
