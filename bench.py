@@ -419,6 +419,7 @@ def zero2_line(a, w, tensors) -> dict:
                                 + (", the last one fused with the update" if fused else ""),
            "shard_params": n, "M": w.M, "tensors": len(w.tensors), "buckets": len(buckets), "micro_batches": K,
            "reduce_streams": NS,
+           "state_stores_streamed": bool(fused and stream_flag),
            "bytes_per_param": bpp, "step_t": hp0["step"],
            "hbm_gbs": round(bpp * n / (avg_ms * 1e-3) / 1e9, 1),
            **({"bucket_phase_ms": round(reduce_ms, 4), "record_ms": round(update_ms, 4)} if fused else
@@ -628,6 +629,8 @@ def main():
         "config": {"workload": w.name, "shard_params": n, "M": w.M, "tensors": len(w.tensors),
                    "bytes_per_param": bpp, "two_pass": w.two_pass or a.amp, "step_t": hp0["step"],
                    "loss_scale": "dynamic, on device" if a.amp else "fixed",
+                   # above this size the library streams the state stores (zero_step decides)
+                   "state_stores_streamed": (not a.composed) and n > z.STREAM_STORES_MIN_PARAMS,
                    **({"form": "composed: zero_shard_reduce, zero_grad_check_norm, zero_adamw_step"}
                       if a.composed else {}),
                    "hbm_gbs": round(bpp * n / (total_ms * 1e-3 / K) / 1e9, 1),
